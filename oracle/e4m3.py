@@ -16,8 +16,10 @@ spell out the bits; they are the OCP OFP8 E4M3 encoding [OFP8]:
 Encoding (the quantizer's second rounding) is round-to-nearest, ties to the
 even code, saturating: magnitudes above 448 (and +-inf) become +-448, as in
 OFP8's saturating conversion mode.  Readings the pages leave open, listed
-here and in the design notes: NaN input encodes to 0x7F with the input's sign
-bit; negative inputs that round to zero keep their sign (0x80).
+here and in the design notes: every NaN input encodes to 0x7F (a NaN's sign
+carries no meaning, and IEEE arithmetic does not fix the sign of a NaN that
+comes out of the quantizer's division); negative inputs that round to zero
+keep their sign (0x80).
 
 Quantization uses one fp32 scale per tensor (one for K, one for V):
 ``code = encode(fp32(x) / fp32(scale))`` -- an IEEE fp32 division (correctly
@@ -68,7 +70,8 @@ def encode(v) -> np.ndarray:
     rounding is the explicit round-half-to-even of the 3-bit mantissa.
     """
     v = np.asarray(v, dtype=np.float32)
-    a = np.abs(v.astype(np.float64))
+    with np.errstate(invalid="ignore"):
+        a = np.abs(v.astype(np.float64))
     sign = (np.signbit(v).astype(np.uint8) << 7).astype(np.uint8)
     code = np.zeros(v.shape, dtype=np.int64)
 
@@ -91,8 +94,8 @@ def encode(v) -> np.ndarray:
     code[normal] = ((e + 7) << 3) | mant
 
     code[saturate] = MAX_CODE
-    code[is_nan] = NAN_CODE
-    return (code.astype(np.uint8) | sign).astype(np.uint8)
+    out = np.asarray(code.astype(np.uint8) | sign, dtype=np.uint8)
+    return np.where(is_nan, np.uint8(NAN_CODE), out).astype(np.uint8)
 
 
 def bf16_bits_to_f32(bits) -> np.ndarray:
@@ -104,9 +107,9 @@ def bf16_bits_to_f32(bits) -> np.ndarray:
 def quantize(x_bf16_bits, scale: float) -> np.ndarray:
     """BF16 values -> e4m3 codes with one fp32 scale: encode(fp32(x) / scale).
 
-    The division is numpy's float32 division (IEEE, correctly rounded); it is
-    deliberately *not* done in float64 -- the GPU divides in fp32 too, and the
-    fp32 quotient is what gets rounded to e4m3.
+    The scale is an fp32 value and the quotient an fp32 value: numpy's float32
+    division (IEEE, correctly rounded) -- deliberately not a float64 or exact
+    division -- and that fp32 quotient is what gets rounded to e4m3.
     """
     x = bf16_bits_to_f32(x_bf16_bits)
     s = np.float32(scale)

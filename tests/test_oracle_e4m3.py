@@ -103,7 +103,7 @@ def test_encode_saturates_and_handles_specials():
     specials = np.array([0.0, -0.0, 1e-30, -1e-30, 2.0 ** -10, -(2.0 ** -10)], np.float32)
     assert list(e4m3.encode(specials)) == [0x00, 0x80, 0x00, 0x80, 0x00, 0x80]
     assert e4m3.encode(np.float32(np.nan)) == 0x7F
-    assert e4m3.encode(-np.float32(np.nan)) == 0xFF
+    assert e4m3.encode(-np.float32(np.nan)) == 0x7F
 
 
 # --- an independent encoder: nearest representable value, exact arithmetic ---
