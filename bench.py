@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""Benchmark: decode-attention tokens/s and effective KV GB/s on one MI355X.
+
+One step = the whole decode hot path for one batch: ``kv_quant_append`` of
+the step's new K/V rows (one token per sequence) followed by
+``paged_decode_attn`` over the paged FP8 e4m3 cache with the page-tag check
+on.  The workload is the batch-32 concurrency case (64 query / 8 KV heads,
+head_dim 128, 64-token pages, context lengths uniform in [4096, 32768], 1% of
+channels scaled x8), synthetic and seeded, resident in HBM before timing.
+
+Printed: one JSON line.  ``value`` = FP8 decode tokens/s (sequences decoded
+per second, one token each, for one attention layer); the BF16-cache run of
+the same workload is reported beside it, plus the tag-check overhead, the
+roofline of the decode kernel (algorithmic bytes per launch / mean launch
+time from HIP events on the launch stream) and the CPU oracle's rate on a
+bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
+WORKLOAD = "conc32"
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_counters.json")
+KERNEL_SOURCES = ["decode_attention_fp8_kv_amd/csrc/decode_attn.hip", "decode_attention_fp8_kv_amd/csrc/common.hpp",
+                  "decode_attention_fp8_kv_amd/csrc/internal.hpp", "decode_attention_fp8_kv_amd/csrc/api.cpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, kv_dtype, flags=None) -> int:
+    """Bytes one decode call must move at minimum for the non-aborted sequences:
+    K and V rows (2*L*Hkv*D*e), q and out (2*Hq*D*2), the page-table entry,
+    page tag and expected tag of every used page (12 B each), one flag byte."""
+    e = 1 if kv_dtype == 0 else 2
+    total = 0
+    for b in range(w.batch):
+        if flags is not None and flags[b]:
+            continue
+        L = int(w.seq_lens[b])
+        total += 2 * L * w.num_kv_heads * w.head_dim * e + 2 * w.num_q_heads * w.head_dim * 2
+        total += (-(-L // w.page_size)) * 12
+    return total + w.batch
+
+
+class Case:
+    """A workload resident on the GPU with its cache filled in one KV dtype."""
+
+    def __init__(self, w, kv_dtype, dev):
+        import torch
+        import decode_attention_fp8_kv_amd as fk
+
+        self.fk, self.torch, self.w, self.kv, self.dev = fk, torch, w, kv_dtype, dev
+        shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+        dt = torch.uint8 if kv_dtype == fk.KV_FP8_E4M3 else torch.bfloat16
+        self.kc = torch.zeros(shape, dtype=dt, device=dev)
+        self.vc = torch.zeros(shape, dtype=dt, device=dev)
+        self.pt = torch.from_numpy(w.page_table).to(dev)
+        self.lens = torch.from_numpy(w.seq_lens).to(dev)
+        self.tags = torch.from_numpy(w.page_tags.view(np.int32)).to(dev)
+        self.exp = torch.from_numpy(w.expected_tags.view(np.int32)).to(dev)
+        self.q = w.q.to(dev).contiguous()
+        self.out = torch.empty_like(self.q)
+        self.flags = torch.empty(w.batch, dtype=torch.uint8, device=dev)
+        self.ws = fk.alloc_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                     w.max_pages, device=dev)
+        fk.kv_quant_append(w.ctx_k, w.ctx_v, w.ctx_seq, w.ctx_pos, self.pt, w.k_scale, w.v_scale,
+                           self.kc, self.vc, kv_dtype)
+        self.new = (w.new_k.contiguous(), w.new_v.contiguous(), w.new_seq, w.new_pos)
+        torch.cuda.synchronize(dev)
+
+    def append(self):
+        nk, nv, ns, npos = self.new
+        self.fk.kv_quant_append(nk, nv, ns, npos, self.pt, self.w.k_scale, self.w.v_scale, self.kc, self.vc,
+                                self.kv)
+
+    def decode(self, tags=True):
+        w = self.w
+        self.fk.paged_decode_attn(self.q, self.kc, self.vc, self.pt, self.lens, self.out, self.flags, self.ws,
+                                  kv_dtype=self.kv, k_scale=w.k_scale, v_scale=w.v_scale,
+                                  page_tags=self.tags if tags else None,
+                                  expected_tags=self.exp if tags else None, softmax_scale=w.softmax_scale)
+
+    def step(self):
+        self.append()
+        self.decode(tags=True)
+
+
+def time_steps(case, steps, warmup):
+    """Warm up, then time exactly `steps` steps between two synchronizations;
+    HIP events on the launch stream bracket each decode launch."""
+    torch = case.torch
+    for _ in range(warmup):
+        case.step()
+    torch.cuda.synchronize(case.dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        case.append()
+        ev[i][0].record()
+        case.decode(tags=True)
+        ev[i][1].record()
+    torch.cuda.synchronize(case.dev)
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return wall, dec_ms
+
+
+def tag_overhead(case, iters=100):
+    """Decode-only launch times with tags on vs off, interleaved."""
+    torch = case.torch
+    on, off = [], []
+    for _ in range(5):
+        case.decode(True)
+        case.decode(False)
+    for i in range(iters):
+        for tags, dst in ((True, on), (False, off)) if i % 2 == 0 else ((False, off), (True, on)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            case.decode(tags)
+            b.record()
+            dst.append((a, b))
+    torch.cuda.synchronize(case.dev)
+    on_ms = np.array([a.elapsed_time(b) for a, b in on])
+    off_ms = np.array([a.elapsed_time(b) for a, b in off])
+    return {
+        "median_on_us": round(float(np.median(on_ms)) * 1e3, 2),
+        "median_off_us": round(float(np.median(off_ms)) * 1e3, 2),
+        "p95_on_us": round(float(np.percentile(on_ms, 95)) * 1e3, 2),
+        "p95_off_us": round(float(np.percentile(off_ms, 95)) * 1e3, 2),
+        "overhead_median": round(float(np.median(on_ms) / np.median(off_ms) - 1.0), 4),
+        "overhead_p95": round(float(np.percentile(on_ms, 95) / np.percentile(off_ms, 95) - 1.0), 4),
+    }
+
+
+def cpu_baseline(w, budget_s=15.0):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    for whole sequences taken in order, time one decode step (append of the new
+    row, tag check, fp64 attention over the page-table-gathered FP8 cache)."""
+    from threadpoolctl import threadpool_info
+
+    from decode_attention_fp8_kv_amd import workloads as W
+    from oracle import paged_attn as pa
+
+    done, elapsed, tokens = [], 0.0, 0
+    for b in range(w.batch):
+        L = int(w.seq_lens[b])
+        n = -(-L // w.page_size)
+        k, v, pos = w.rows_of(b)
+        shape = (n, w.num_kv_heads, w.page_size, w.head_dim)
+        kc, vc = np.zeros(shape, np.uint8), np.zeros(shape, np.uint8)
+        mini_pt = np.arange(n, dtype=np.int32)[None, :]
+        ctx = pos.numpy() < L - 1                                   # the cache before this step
+        pa.append(W.bits_u16(k[ctx]), W.bits_u16(v[ctx]), np.zeros(int(ctx.sum()), np.int32), pos.numpy()[ctx],
+                  mini_pt, w.k_scale, w.v_scale, kc, vc)
+        tags = w.page_tags[w.page_table[b, :n]]
+        exp = w.expected_tags[b:b + 1, :n]
+        q = W.bits_u16(w.q[b:b + 1])
+        t0 = time.perf_counter()
+        pa.append(W.bits_u16(k[~ctx]), W.bits_u16(v[~ctx]), np.zeros(int((~ctx).sum()), np.int32),
+                  pos.numpy()[~ctx], mini_pt, w.k_scale, w.v_scale, kc, vc)
+        flags = pa.abort_flags(mini_pt, np.array([L]), w.page_size, n, tags, exp)
+        pa.decode_attention(q, kc, vc, pa.KV_FP8_E4M3, w.k_scale, w.v_scale, mini_pt, np.array([L]),
+                            w.softmax_scale, flags=flags)
+        elapsed += time.perf_counter() - t0
+        done.append(b)
+        tokens += L
+        if elapsed >= budget_s:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(len(done) / elapsed, 3),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(done)} of {w.batch} sequences ({tokens} cached tokens), one decode step each, "
+                  f"{elapsed:.1f} s of CPU time; numpy fp64 with {threads} BLAS threads",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_fp8_kv_amd as fk
+    from decode_attention_fp8_kv_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    fk.load_library()
+    w = W.make(WORKLOAD, device=dev)
+    res = {}
+    for kv, name in ((fk.KV_FP8_E4M3, "fp8"), (fk.KV_BF16, "bf16")):
+        if name == "bf16" and args.no_bf16:
+            continue
+        case = Case(w, kv, dev)
+        torch.cuda.synchronize(dev)
+        wall, dec_ms = time_steps(case, args.steps, args.warmup)
+        flags = case.flags.cpu().numpy()
+        alg = algorithmic_bytes(w, kv, flags)
+        ok = int((flags == 0).sum())
+        mean_us = float(dec_ms.mean()) * 1e3
+        res[name] = {
+            "value": ok * args.steps / wall,
+            "ms_per_step": wall / args.steps * 1e3,
+            "decode_mean_us": mean_us,
+            "decode_median_us": float(np.median(dec_ms)) * 1e3,
+            "decode_p95_us": float(np.percentile(dec_ms, 95)) * 1e3,
+            "alg_bytes": alg,
+            "gbps": alg / (mean_us * 1e-6) / 1e9,
+            "aborted": int(w.batch - ok),
+        }
+        if name == "fp8":
+            res["tags"] = tag_overhead(case)
+        del case
+        torch.cuda.empty_cache()
+
+    f = res["fp8"]
+    traffic = None
+    if os.path.exists(PROFILE_COUNTERS):
+        with open(PROFILE_COUNTERS) as fh:
+            prof = json.load(fh)
+        if prof.get("kernel_source_hash") == kernel_source_hash():
+            traffic = prof.get("traffic_bytes_per_launch")
+    line = {
+        "metric": "decode-attn tokens/s + effective KV GB/s (% HBM peak), FP8 vs BF16 KV, 1 GPU",
+        "value": round(f["value"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(f["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded; K/V/Q ~ N(0,1) bf16, 1% channels x8, random page permutation)",
+        "config": {
+            "workload": "conc32: batch 32, 64 q heads / 8 KV heads, head_dim 128, page 64, context "
+                        "U[4096,32768] + 1 appended token per step, page-tag check on",
+            "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "page_size": w.page_size, "context_tokens": int(w.seq_lens.sum()),
+            "parallelism": "single GPU",
+        },
+        "effective_kv_gbps": round(f["gbps"], 1),
+        "pct_hbm_peak": round(100.0 * f["gbps"] / PEAK_HBM_GBPS, 2),
+        "decode_us": {"mean": round(f["decode_mean_us"], 2), "median": round(f["decode_median_us"], 2),
+                      "p95": round(f["decode_p95_us"], 2)},
+        "roofline": {
+            "kernel": "decode_kernel<fp8,128,16,mfma> (paged_decode_attn)",
+            "bound": "hbm",
+            "achieved": round(f["gbps"], 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(f["gbps"] / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+        },
+        "tag_check": res.get("tags"),
+    }
+    if "bf16" in res:
+        b = res["bf16"]
+        line["bf16"] = {"value": round(b["value"], 1), "unit": "tokens/s", "ms_per_step": round(b["ms_per_step"], 4),
+                        "effective_kv_gbps": round(b["gbps"], 1),
+                        "pct_hbm_peak": round(100.0 * b["gbps"] / PEAK_HBM_GBPS, 2),
+                        "decode_mean_us": round(b["decode_mean_us"], 2)}
+        line["fp8_over_bf16_tokens_per_s"] = round(f["value"] / b["value"], 3)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

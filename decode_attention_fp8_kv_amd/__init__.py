@@ -1,0 +1,183 @@
+"""Paged decode attention over an FP8 e4m3 KV cache with page-tag checks, for
+AMD Instinct MI355X (gfx950).
+
+This package is a thin binding over the C ABI in ``include/fp8kv.h``
+(``libfp8kv.so``, built in-tree by ``decode_attention_fp8_kv_amd.build``).
+The functions below only marshal torch tensors into pointers and sizes;
+every step of the computation runs in the library's HIP kernels.  If the
+library is missing, every call raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "KV_FP8_E4M3", "KV_BF16", "ABORT_TAG_MISMATCH", "ABORT_BAD_METADATA", "Fp8KvError",
+    "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
+    "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
+]
+
+KV_FP8_E4M3 = 0
+KV_BF16 = 1
+ABORT_TAG_MISMATCH = 1
+ABORT_BAD_METADATA = 2
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libfp8kv.so")
+_lib = None
+
+
+class Fp8KvError(RuntimeError):
+    """A negative status from the library."""
+
+    def __init__(self, fn: str, status: int, text: str, hip: str):
+        msg = f"{fn} failed with status {status}: {text}"
+        if hip:
+            msg += f" ({hip})"
+        super().__init__(msg)
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load ``libfp8kv.so`` once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(
+            f"{lib_path} is missing: build it with `python -m decode_attention_fp8_kv_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(lib_path)
+    c = ctypes
+    vp, i32, f32, sz = c.c_void_p, c.c_int32, c.c_float, c.c_size_t
+    lib.fp8kv_abi_version.restype = c.c_int
+    lib.fp8kv_abi_version.argtypes = []
+    lib.fp8kv_status_string.restype = c.c_char_p
+    lib.fp8kv_status_string.argtypes = [c.c_int]
+    lib.fp8kv_last_hip_error.restype = c.c_char_p
+    lib.fp8kv_last_hip_error.argtypes = []
+    lib.kv_quant_append.restype = c.c_int
+    lib.kv_quant_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, i32, i32, i32, i32, i32,
+                                    i32, vp]
+    lib.paged_decode_attn_workspace_size.restype = sz
+    lib.paged_decode_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.paged_decode_attn_path.restype = c.c_int
+    lib.paged_decode_attn_path.argtypes = [i32, i32]
+    lib.paged_decode_attn.restype = c.c_int
+    lib.paged_decode_attn.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, vp, sz, i32, i32,
+                                      i32, i32, i32, i32, f32, i32, vp]
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().fp8kv_abi_version()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        lib = load_library()
+        raise Fp8KvError(fn, status, lib.fp8kv_status_string(status).decode(),
+                         lib.fp8kv_last_hip_error().decode())
+
+
+def _ptr(t, dtypes, name, device=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    return t.data_ptr()
+
+
+def _stream_handle(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_BF16 = (torch.bfloat16,)
+_I32 = (torch.int32,)
+_U32 = (torch.int32, torch.uint32)
+_CACHE = {KV_FP8_E4M3: (torch.uint8, torch.float8_e4m3fn), KV_BF16: (torch.bfloat16,)}
+
+
+def kv_quant_append(k_new, v_new, row_seq, row_pos, page_table, k_scale, v_scale, k_cache, v_cache,
+                    kv_dtype=KV_FP8_E4M3, stream=None):
+    """Write rows ``k_new/v_new [n_rows, Hkv, D]`` into the paged caches.
+
+    See ``kv_quant_append`` in ``include/fp8kv.h`` for the exact semantics.
+    ``k_cache/v_cache``: ``[num_pages, Hkv, page_size, D]`` uint8 (FP8) or bf16.
+    """
+    dev = k_cache.device
+    n_rows, hkv, d = k_new.shape
+    num_pages, hkv_c, page_size, d_c = k_cache.shape
+    if (hkv, d) != (hkv_c, d_c) or v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
+        raise ValueError("shape mismatch between rows and caches")
+    if row_seq.numel() != n_rows or row_pos.numel() != n_rows:
+        raise ValueError("row_seq/row_pos must have n_rows entries")
+    batch, max_pages = page_table.shape
+    status = load_library().kv_quant_append(
+        _ptr(k_new, _BF16, "k_new", dev), _ptr(v_new, _BF16, "v_new", dev),
+        _ptr(row_seq, _I32, "row_seq", dev), _ptr(row_pos, _I32, "row_pos", dev),
+        _ptr(page_table, _I32, "page_table", dev), batch, max_pages, float(k_scale), float(v_scale),
+        _ptr(k_cache, _CACHE[kv_dtype], "k_cache", dev), _ptr(v_cache, _CACHE[kv_dtype], "v_cache", dev),
+        num_pages, n_rows, hkv, d, page_size, kv_dtype, _stream_handle(dev, stream))
+    _check("kv_quant_append", status)
+
+
+def paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages,
+                                     num_splits=0) -> int:
+    return int(load_library().paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                               page_size, max_pages, num_splits))
+
+
+def paged_decode_attn_path(num_q_heads, num_kv_heads) -> int:
+    return int(load_library().paged_decode_attn_path(num_q_heads, num_kv_heads))
+
+
+def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, num_splits=0,
+                    device="cuda"):
+    """A zero-filled workspace of the size the library asks for (allocated by torch)."""
+    n = paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages,
+                                         num_splits)
+    if n == 0:
+        raise ValueError("invalid sizes for a workspace")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flags, workspace, *,
+                      kv_dtype=KV_FP8_E4M3, k_scale=1.0, v_scale=1.0, page_tags=None, expected_tags=None,
+                      softmax_scale=None, num_splits=0, stream=None):
+    """One decode step of attention; writes ``out`` (bf16) and ``abort_flags`` (uint8).
+
+    See ``paged_decode_attn`` in ``include/fp8kv.h`` for the exact semantics.
+    """
+    dev = q.device
+    batch, hq, d = q.shape
+    num_pages, hkv, page_size, _ = k_cache.shape
+    max_pages = page_table.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out.shape != q.shape or abort_flags.numel() != batch or page_table.shape[0] != batch:
+        raise ValueError("shape mismatch")
+    status = load_library().paged_decode_attn(
+        _ptr(q, _BF16, "q", dev), _ptr(k_cache, _CACHE[kv_dtype], "k_cache", dev),
+        _ptr(v_cache, _CACHE[kv_dtype], "v_cache", dev), kv_dtype, float(k_scale), float(v_scale),
+        _ptr(page_table, _I32, "page_table", dev), max_pages, _ptr(seq_lens, _I32, "seq_lens", dev),
+        _ptr(page_tags, _U32, "page_tags", dev), _ptr(expected_tags, _U32, "expected_tags", dev),
+        _ptr(out, _BF16, "out", dev), _ptr(abort_flags, (torch.uint8,), "abort_flags", dev),
+        _ptr(workspace, (torch.uint8,), "workspace", dev), workspace.numel(),
+        batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_splits),
+        _stream_handle(dev, stream))
+    _check("paged_decode_attn", status)

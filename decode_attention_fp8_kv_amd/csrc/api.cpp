@@ -1,0 +1,222 @@
+// C-ABI entry points declared in include/fp8kv.h: host-side argument checks,
+// the work plan, and launches on the caller's stream.  No entry point
+// allocates, synchronizes or reads device memory.
+#include "fp8kv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace fp8kv {
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+int record_hip(hipError_t e) {
+  if (e == hipSuccess) return FP8KV_OK;
+  std::snprintf(g_last_hip_error, sizeof g_last_hip_error, "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+  return FP8KV_ERR_LAUNCH;
+}
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+
+int log2_page_size(int32_t ps) {
+  if (ps < 16 || ps > 256 || (ps & (ps - 1)) != 0) return -1;
+  int l = 0;
+  while ((1 << l) < ps) ++l;
+  return l;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
+
+constexpr int64_t kTargetBlocks = 8192;  // enough blocks to keep 256 CUs busy through a ragged tail
+constexpr int kMaxSplits = 256;          // bound of the final merge's per-split weight table
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages,
+                      int32_t num_splits) {
+  const int64_t max_tokens = (int64_t)max_pages * page_size;
+  const int64_t max_tiles = (max_tokens + kTileTokens - 1) / kTileTokens;
+  int64_t splits;
+  if (num_splits > 0) {
+    splits = num_splits;
+  } else {
+    const int64_t pairs = (int64_t)batch * num_kv_heads;
+    splits = (kTargetBlocks + pairs - 1) / pairs;
+    // keep at least one tile per wave in a split when the context allows
+    splits = std::min<int64_t>(splits, std::max<int64_t>(1, max_tiles / kWavesPerBlock));
+  }
+  splits = std::max<int64_t>(1, std::min<int64_t>({splits, max_tiles, (int64_t)kMaxSplits}));
+  SplitPlan plan;
+  plan.tiles_per_split = (int32_t)((max_tiles + splits - 1) / splits);
+  plan.splits = (int32_t)((max_tiles + plan.tiles_per_split - 1) / plan.tiles_per_split);
+  return plan;
+}
+
+WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t splits) {
+  const size_t pairs = (size_t)batch * num_kv_heads;
+  const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  WorkspaceLayout w;
+  w.counters = 0;
+  w.split_status = round_up(pairs * sizeof(uint32_t), 256);
+  w.split_ml = w.split_status + round_up(pairs * splits * sizeof(uint32_t), 256);
+  w.split_acc = w.split_ml + round_up(pairs * splits * group * 2 * sizeof(float), 256);
+  w.total = w.split_acc + round_up(pairs * splits * group * head_dim * sizeof(float), 256);
+  return w;
+}
+
+}  // namespace fp8kv
+
+using namespace fp8kv;
+
+extern "C" {
+
+int fp8kv_abi_version(void) { return FP8KV_ABI_VERSION; }
+
+const char* fp8kv_status_string(int status) {
+  switch (status) {
+    case FP8KV_OK: return "ok";
+    case FP8KV_ERR_NULL: return "a required pointer is NULL";
+    case FP8KV_ERR_SHAPE: return "invalid size (non-positive, heads not divisible, or too large)";
+    case FP8KV_ERR_UNSUPPORTED: return "unsupported head_dim, page_size, GQA group or kv_dtype";
+    case FP8KV_ERR_WORKSPACE: return "workspace too small";
+    case FP8KV_ERR_SCALE: return "scale not finite and positive";
+    case FP8KV_ERR_TAGS: return "page_tags and expected_tags must both be NULL or both be set";
+    case FP8KV_ERR_LAUNCH: return "HIP launch failed (see fp8kv_last_hip_error)";
+    case FP8KV_ERR_ALIGN: return "a pointer is not aligned as required";
+    default: return "unknown status";
+  }
+}
+
+const char* fp8kv_last_hip_error(void) { return g_last_hip_error; }
+
+int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
+                    const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
+                    void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* stream) {
+  if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+  if (n_rows < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
+  if (!supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
+  const int l2ps = log2_page_size(page_size);
+  if (l2ps < 0) return FP8KV_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages * page_size > INT32_MAX) return FP8KV_ERR_SHAPE;
+  if (n_rows == 0) return FP8KV_OK;
+  if (!k_new || !v_new || !row_seq || !row_pos || !page_table || !k_cache || !v_cache) return FP8KV_ERR_NULL;
+  if (kv_dtype == FP8KV_KV_FP8_E4M3 && (!finite_positive(k_scale) || !finite_positive(v_scale)))
+    return FP8KV_ERR_SCALE;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return FP8KV_ERR_ALIGN;
+
+  AppendParams p;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.row_seq = row_seq;
+  p.row_pos = row_pos;
+  p.page_table = page_table;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.batch = batch;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  p.n_rows = n_rows;
+  p.num_kv_heads = num_kv_heads;
+  p.head_dim = head_dim;
+  p.log2_page_size = l2ps;
+  return record_hip(launch_quant_append(p, kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t page_size, int32_t max_pages, int32_t num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_splits < 0) return 0;
+  if (num_q_heads % num_kv_heads != 0 || !supported_head_dim(head_dim) || log2_page_size(page_size) < 0) return 0;
+  const SplitPlan plan = plan_splits(batch, num_kv_heads, page_size, max_pages, num_splits);
+  return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, plan.splits).total;
+}
+
+int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0) return -1;
+  const char* force = std::getenv("FP8KV_FORCE_PATH");
+  if (force && std::strcmp(force, "mfma") == 0) return 1;
+  if (force && std::strcmp(force, "valu") == 0 && num_q_heads / num_kv_heads <= 4) return 0;
+  return num_q_heads / num_kv_heads >= 5 ? 1 : 0;
+}
+
+int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, float k_scale,
+                      float v_scale, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                      const uint32_t* page_tags, const uint32_t* expected_tags, uint16_t* out, uint8_t* abort_flags,
+                      void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+                      float softmax_scale, int32_t num_splits, void* stream) {
+  if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0)
+    return FP8KV_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return FP8KV_ERR_SHAPE;
+  if (batch > 65535 || num_kv_heads > 65535) return FP8KV_ERR_SHAPE;
+  const int32_t group = num_q_heads / num_kv_heads;
+  if (group > kMaxGroup || !supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
+  const int l2ps = log2_page_size(page_size);
+  if (l2ps < 0) return FP8KV_ERR_UNSUPPORTED;
+  if ((int64_t)max_pages * page_size > INT32_MAX) return FP8KV_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !abort_flags || !workspace)
+    return FP8KV_ERR_NULL;
+  if ((page_tags == nullptr) != (expected_tags == nullptr)) return FP8KV_ERR_TAGS;
+  if (kv_dtype == FP8KV_KV_FP8_E4M3 && (!finite_positive(k_scale) || !finite_positive(v_scale)))
+    return FP8KV_ERR_SCALE;
+  if (!std::isfinite(softmax_scale)) return FP8KV_ERR_SCALE;
+  if (!aligned(q, 16) || !aligned(out, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(workspace, 256))
+    return FP8KV_ERR_ALIGN;
+  const SplitPlan plan = plan_splits(batch, num_kv_heads, page_size, max_pages, num_splits);
+  const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, plan.splits);
+  if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;
+
+  const double log2e = 1.4426950408889634;
+  DecodeParams p;
+  p.q = q;
+  p.k_cache = static_cast<const uint8_t*>(k_cache);
+  p.v_cache = static_cast<const uint8_t*>(v_cache);
+  p.page_table = page_table;
+  p.seq_lens = seq_lens;
+  p.page_tags = page_tags;
+  p.expected_tags = expected_tags;
+  p.out = out;
+  p.abort_flags = abort_flags;
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.counters = reinterpret_cast<uint32_t*>(base + ws.counters);
+  p.split_status = reinterpret_cast<uint32_t*>(base + ws.split_status);
+  p.split_ml = reinterpret_cast<float*>(base + ws.split_ml);
+  p.split_acc = reinterpret_cast<float*>(base + ws.split_acc);
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  p.log2_page_size = l2ps;
+  p.tiles_per_split = plan.tiles_per_split;
+  p.splits = plan.splits;
+  if (kv_dtype == FP8KV_KV_FP8_E4M3) {
+    p.qk_scale_log2 = (float)((double)softmax_scale * (double)k_scale * log2e);
+    p.v_scale = v_scale;
+  } else {
+    p.qk_scale_log2 = (float)((double)softmax_scale * log2e);
+    p.v_scale = 1.0f;
+  }
+  const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
+  return record_hip(launch_decode(p, kv_dtype, head_dim, mfma, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,792 @@
+// paged_decode_attn kernels for gfx950: split-K (flash-decoding) decode
+// attention over a paged K/V cache held as e4m3 (or BF16), with the page-tag
+// check done before any page's contents are used.
+//
+// What is computed (source pages: "Cloudflare tối ưu hóa Kimi và GLM trên
+// Workers AI", section "Lượng tử hóa KV cache" -- the attention kernel reads
+// an FP8 e4m3 cache and converts values as it reads them; "ترفندهای کلادفلر
+// برای جا دادن مدل‌های غول‌پیکر تو GPU", third technique, and "Tối ưu hóa mô
+// hình AI quy mô lớn", section "Bảo vệ tính toàn vẹn của KV Cache" -- each
+// page carries a tag that changes on reallocation, checked before the page
+// is read, a mismatch aborting the request):
+//
+//   out[b][h] = sum_t softmax_t(scale * <q[b][h], k_t>) v_t
+//
+// over the L = seq_lens[b] tokens of KV head h / G, read through the page
+// table; nothing is written for a sequence whose pages fail the check.
+//
+// Work decomposition
+// ------------------
+// grid = (splits, num_kv_heads, batch), 256 threads (4 waves) per block.
+// A block owns `tiles_per_split` consecutive 64-token tiles of one
+// (sequence, KV head); its 4 waves take every 4th tile and each keeps its
+// own online-softmax state (running max m, sum l, unnormalized acc).  The
+// waves merge through LDS; the block then either writes the output directly
+// (one split) or stores its partial (m, l, acc, status) in the workspace and
+// bumps an arrival counter -- the block that arrives last for its
+// (sequence, KV head) merges all partials (log-sum-exp) and writes the
+// output and the abort flag, then resets the counter to zero.
+//
+// Per wave and tile (MFMA family, group of 5..16 query heads per KV head):
+//   * K rows: lane l loads a quarter of one token's row (bytes of dims
+//     [q*D/4, (q+1)*D/4), q = l/16) for 4 token blocks; 16 lanes cover one
+//     full row, so every load instruction reads whole 128-byte lines.
+//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 dims of
+//     K (e4m3 -> bf16 exact in registers), B = 32 dims x 16 query heads.  The
+//     dims a lane contributes at each k-step are relabelled consistently in
+//     A and B, which is what lets a lane read 32 contiguous bytes.
+//   * Tokens are relabelled so that the C layout of S^T (lane l holds head
+//     l%16 for 4 tokens) is exactly the B layout P^T needs for PV -- no data
+//     moves between lanes between the two products.
+//   * O^T = V^T P^T with v_mfma_f32_16x16x32_f16 (FP8: e4m3 -> f16 exact,
+//     P rounded to f16) or _bf16 (BF16 cache): lane l loads 16 tokens x D/16
+//     contiguous dims of V; a byte (or half-word) transpose in registers
+//     (v_perm_b32) builds the A operand.  The accumulator layout puts head
+//     l%16 in lane l, the same lane that owns its softmax state.
+//   * Softmax max/sum across the 4 lane groups: wave shuffles.
+// VALU family (groups of 1..4): lane = (token slot, dim chunk); dot products
+// with v_dot2_f32_bf16 and fp32 FMA, octet sums through DPP.
+//
+// Scales: k_scale * softmax_scale * log2(e) multiplies the fp32 scores and
+// v_scale the final output, so dequantization itself adds no rounding.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace fp8kv {
+namespace {
+
+constexpr uint32_t kAbortTag = 1u;
+constexpr uint32_t kAbortMeta = 2u;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kMaxCombineSplits = 256;
+
+template <int D>
+struct MergeLds {
+  float m[kWavesPerBlock][kMaxGroup];
+  float l[kWavesPerBlock][kMaxGroup];
+  union {
+    float acc[kWavesPerBlock][kMaxGroup][D];
+    float w[kMaxCombineSplits][kMaxGroup];  // final combine: per-split weights
+  };
+  float head_m[kMaxGroup];
+  float head_inv_l[kMaxGroup];
+  uint32_t status[kWavesPerBlock];
+  uint32_t flag;
+};
+static_assert(sizeof(float) * kWavesPerBlock * kMaxGroup * 64 >= sizeof(float) * kMaxCombineSplits * kMaxGroup,
+              "combine weights must fit in the merge buffer");
+
+// ------------------------------------------------------------------------
+// Geometry of one element type / head size.
+// ------------------------------------------------------------------------
+template <int KV, int D>
+struct Geo {
+  static constexpr int ESZ = KV == 0 ? 1 : 2;   // bytes per cache element
+  static constexpr int ROW = D * ESZ;           // bytes per (token, KV head) row
+  // MFMA family
+  static constexpr int KSTEPS = D / 32;         // QK k-steps of 32 dims
+  static constexpr int NB = D / 16;             // PV output blocks of 16 dims
+  static constexpr int KQ = D / 4 * ESZ;        // K bytes per lane per token (a quarter row)
+  static constexpr int KQV = KQ / 16;           // 16-byte loads per quarter row
+  static constexpr int VW = NB * ESZ / 4;       // V words (4 bytes) per lane per token
+  // VALU family
+  static constexpr int DC = D / 8;              // dims per lane
+  static constexpr int CW = DC * ESZ / 4;       // words per lane per token
+};
+
+// Load N consecutive 4-byte words with the widest aligned vector loads.
+template <int N>
+__device__ __forceinline__ void load_words(const uint8_t* src, uint32_t* dst) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + 4 * i);
+      dst[i] = x[0]; dst[i + 1] = x[1]; dst[i + 2] = x[2]; dst[i + 3] = x[3];
+    }
+  } else if constexpr (N == 2) {
+    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
+    dst[0] = x[0]; dst[1] = x[1];
+  } else {
+    static_assert(N == 1, "unsupported word count");
+    dst[0] = *reinterpret_cast<const uint32_t*>(src);
+  }
+}
+
+// ------------------------------------------------------------------------
+// Page walk: the wave's page list for a round of its tiles.
+// ------------------------------------------------------------------------
+struct PageRound {
+  int pid;       // lane j: physical page of wave page j (a safe substitute where unused)
+  int log2ps;
+  int ppt_log2;  // log2(pages per tile) when pages are smaller than a tile, else 0
+};
+
+// Physical page holding 16-token group `grp16` (0..3) of the round's tile `i`.
+__device__ __forceinline__ int page_of(const PageRound& pr, int i, int grp16) {
+  if (pr.log2ps >= 6) return __builtin_amdgcn_readlane(pr.pid, i);
+  return __shfl(pr.pid, (i << pr.ppt_log2) + (grp16 >> (pr.log2ps - 4)));
+}
+
+__device__ __forceinline__ const uint8_t* row_ptr(const uint8_t* cache, int pid, int g, int hkv,
+                                                  int log2ps, int slot, int row_bytes) {
+  return cache + ((((int64_t)pid * hkv + g) << log2ps) + slot) * (int64_t)row_bytes;
+}
+
+// ------------------------------------------------------------------------
+// MFMA family.
+// ------------------------------------------------------------------------
+template <int KV, int D>
+struct MfmaTile {
+  using G_ = Geo<KV, D>;
+  uint32_t k[4][G_::KQ / 4];   // token block bb: this lane's quarter row
+  uint32_t v[16][G_::VW];      // 16 tokens: this lane's D/16 dims
+};
+
+template <int KV, int D>
+struct MfmaState {
+  float m, l;
+  f32x4_t acc[Geo<KV, D>::NB];
+  bf16x8_t q[Geo<KV, D>::KSTEPS];
+};
+
+template <int KV, int D>
+__device__ __forceinline__ void mfma_load_k(MfmaTile<KV, D>& t, const uint8_t* kp) {
+  using G_ = Geo<KV, D>;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) load_words<G_::KQ / 4>(kp + bb * 4 * G_::ROW, t.k[bb]);
+}
+template <int KV, int D>
+__device__ __forceinline__ void mfma_load_v(MfmaTile<KV, D>& t, const uint8_t* vp) {
+  using G_ = Geo<KV, D>;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) load_words<G_::VW>(vp + i * G_::ROW, t.v[i]);
+}
+
+// S^T for the tile's 64 tokens: s[bb][r] = score of token 16*(lane/16) + 4*bb + r
+// for query head lane%16 (unscaled).
+template <int KV, int D>
+__device__ __forceinline__ void mfma_qk(const MfmaTile<KV, D>& t, const MfmaState<KV, D>& st, f32x4_t s[4]) {
+  using G_ = Geo<KV, D>;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < G_::KSTEPS; ++kk) {
+      bf16x8_t a;
+      if constexpr (KV == 0) {
+        a = e4m3x8_to_bf16x8(t.k[bb][2 * kk], t.k[bb][2 * kk + 1]);
+      } else {
+        u32x4_t w = {t.k[bb][4 * kk], t.k[bb][4 * kk + 1], t.k[bb][4 * kk + 2], t.k[bb][4 * kk + 3]};
+        a = __builtin_bit_cast(bf16x8_t, w);
+      }
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, st.q[kk], c, 0, 0, 0);
+    }
+    s[bb] = c;
+  }
+}
+
+// Online softmax update for the tile and O^T += V^T P^T.
+template <int KV, int D>
+__device__ __forceinline__ void mfma_softmax_pv(MfmaTile<KV, D>& t, MfmaState<KV, D>& st, f32x4_t s[4],
+                                                int valid, float scale_log2, int lane) {
+  using G_ = Geo<KV, D>;
+  const int vg = lane >> 4;
+  float mt = kNegInf;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = s[bb][r] * scale_log2;
+      if (valid < kTileTokens && 16 * vg + 4 * bb + r >= valid) x = kNegInf;
+      s[bb][r] = x;
+      mt = __builtin_fmaxf(mt, x);
+    }
+  mt = xor_max(mt, 16);
+  mt = xor_max(mt, 32);
+  const float m_new = __builtin_fmaxf(st.m, mt);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  st.m = m_new;
+  st.l *= alpha;
+#pragma unroll
+  for (int nb = 0; nb < G_::NB; ++nb) st.acc[nb] *= alpha;
+  float pr[4][4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pr[bb][r] = fast_exp2(s[bb][r] - m_use);
+      st.l += pr[bb][r];
+    }
+
+  // Rows past the sequence end may hold anything (even NaN codes): zero them.
+  if (valid < kTileTokens) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (16 * vg + i >= valid)
+#pragma unroll
+        for (int w = 0; w < G_::VW; ++w) t.v[i][w] = 0u;
+  }
+
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    if constexpr (KV == 0) {
+      // B = P^T (f16): slots 0..3 = tokens 8ks+0..3, 4..7 = tokens 8ks+4..7 of this lane group
+      f16x8_t bop;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bop[r] = (_Float16)pr[2 * ks][r];
+        bop[4 + r] = (_Float16)pr[2 * ks + 1][r];
+      }
+      // A = V^T: byte-transpose 8 tokens x (4 dims per word) -> per dim 8 tokens
+#pragma unroll
+      for (int w = 0; w < G_::VW; ++w) {
+        uint32_t lo[4], hi[4];
+        transpose4x4_bytes(t.v[8 * ks + 0][w], t.v[8 * ks + 1][w], t.v[8 * ks + 2][w], t.v[8 * ks + 3][w],
+                           lo[0], lo[1], lo[2], lo[3]);
+        transpose4x4_bytes(t.v[8 * ks + 4][w], t.v[8 * ks + 5][w], t.v[8 * ks + 6][w], t.v[8 * ks + 7][w],
+                           hi[0], hi[1], hi[2], hi[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f16x8_t aop = e4m3x8_to_f16x8(lo[e], hi[e]);
+          st.acc[4 * w + e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop, st.acc[4 * w + e], 0, 0, 0);
+        }
+      }
+    } else {
+      bf16x8_t bop;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bop[r] = (__bf16)pr[2 * ks][r];
+        bop[4 + r] = (__bf16)pr[2 * ks + 1][r];
+      }
+      // word w of a token holds dims (2w, 2w+1); pair tokens for each dim
+#pragma unroll
+      for (int w = 0; w < G_::VW; ++w) {
+        u32x4_t a0, a1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a0[j] = pair_lo16(t.v[8 * ks + 2 * j][w], t.v[8 * ks + 2 * j + 1][w]);
+          a1[j] = pair_hi16(t.v[8 * ks + 2 * j][w], t.v[8 * ks + 2 * j + 1][w]);
+        }
+        st.acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), bop,
+                                                                st.acc[2 * w], 0, 0, 0);
+        st.acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), bop,
+                                                                    st.acc[2 * w + 1], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// VALU family.
+// ------------------------------------------------------------------------
+template <int KV, int D>
+struct ValuTile {
+  uint32_t k[8][Geo<KV, D>::CW];
+  uint32_t v[8][Geo<KV, D>::CW];
+};
+
+template <int KV, int D, int GM>
+struct ValuState {
+  float m[GM], l[GM];
+  float acc[GM][Geo<KV, D>::DC];
+  uint32_t q2[GM][Geo<KV, D>::DC / 2];  // bf16 pairs of the query
+};
+
+template <int KV, int D>
+__device__ __forceinline__ void valu_load(ValuTile<KV, D>& t, const uint8_t* kp, const uint8_t* vp) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) load_words<Geo<KV, D>::CW>(kp + u * Geo<KV, D>::ROW, t.k[u]);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) load_words<Geo<KV, D>::CW>(vp + u * Geo<KV, D>::ROW, t.v[u]);
+}
+
+// bf16 pairs of one token's DC dims
+template <int KV, int D>
+__device__ __forceinline__ void valu_pairs(const uint32_t* w, uint32_t* out) {
+  if constexpr (KV == 0) {
+#pragma unroll
+    for (int i = 0; i < Geo<KV, D>::CW; ++i) {
+      out[2 * i] = e4m3x2_to_bf16x2<false>(w[i]);
+      out[2 * i + 1] = e4m3x2_to_bf16x2<true>(w[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < Geo<KV, D>::CW; ++i) out[i] = w[i];
+  }
+}
+
+template <int KV, int D, int GM>
+__device__ __forceinline__ void valu_qk(const ValuTile<KV, D>& t, const ValuState<KV, D, GM>& st,
+                                        float s[8][GM]) {
+  constexpr int DC = Geo<KV, D>::DC;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    uint32_t kp[DC / 2];
+    valu_pairs<KV, D>(t.k[u], kp);
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < DC / 2; ++i)
+        a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, st.q2[h][i]),
+                                            __builtin_bit_cast(bf16x2_t, kp[i]), a, false);
+      s[u][h] = octet_sum(a);
+    }
+  }
+}
+
+template <int KV, int D, int GM>
+__device__ __forceinline__ void valu_softmax_pv(ValuTile<KV, D>& t, ValuState<KV, D, GM>& st, float s[8][GM],
+                                                int valid, float scale_log2, int lane) {
+  constexpr int DC = Geo<KV, D>::DC;
+  const int ts = lane >> 3;
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    float mt = kNegInf;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float x = s[u][h] * scale_log2;
+      if (valid < kTileTokens && 8 * ts + u >= valid) x = kNegInf;
+      s[u][h] = x;
+      mt = __builtin_fmaxf(mt, x);
+    }
+    const float m_new = __builtin_fmaxf(st.m[h], mt);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = fast_exp2(st.m[h] - m_use);
+    st.m[h] = m_new;
+    st.l[h] *= alpha;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) st.acc[h][i] *= alpha;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s[u][h] = fast_exp2(s[u][h] - m_use);
+      st.l[h] += s[u][h];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    float vf[DC];
+    if constexpr (KV == 0) {
+#pragma unroll
+      for (int i = 0; i < Geo<KV, D>::CW; ++i) e4m3x4_to_f32(t.v[u][i], vf + 4 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Geo<KV, D>::CW; ++i) {
+        vf[2 * i] = bf16_bits_to_f32(t.v[u][i] & 0xFFFFu);
+        vf[2 * i + 1] = __builtin_bit_cast(float, t.v[u][i] & 0xFFFF0000u);
+      }
+    }
+    if (valid < kTileTokens && 8 * ts + u >= valid) {
+#pragma unroll
+      for (int i = 0; i < DC; ++i) vf[i] = 0.f;
+    }
+#pragma unroll
+    for (int h = 0; h < GM; ++h)
+#pragma unroll
+      for (int i = 0; i < DC; ++i) st.acc[h][i] = __builtin_fmaf(s[u][h], vf[i], st.acc[h][i]);
+  }
+}
+
+// ------------------------------------------------------------------------
+// One wave: walk its tiles (every 4th tile of the block's chunk), checking
+// the pages of each round before any of their contents are used.
+// ------------------------------------------------------------------------
+template <int KV, int D, int GM, bool MFMA>
+struct WaveState;
+template <int KV, int D, int GM>
+struct WaveState<KV, D, GM, true> { using T = MfmaState<KV, D>; using Tile = MfmaTile<KV, D>; };
+template <int KV, int D, int GM>
+struct WaveState<KV, D, GM, false> { using T = ValuState<KV, D, GM>; using Tile = ValuTile<KV, D>; };
+
+template <int KV, int D, int GM, bool MFMA>
+__device__ __forceinline__ void tile_pointers(const DecodeParams& p, const PageRound& pr, int i, int tile_abs,
+                                              int g, int lane, const uint8_t*& kp, const uint8_t*& vp) {
+  using G_ = Geo<KV, D>;
+  const int ps_mask = (1 << pr.log2ps) - 1;
+  const int base_tok = tile_abs << 6;
+  if constexpr (MFMA) {
+    const int kg = (lane & 15) >> 2;
+    const int ktok = 16 * kg + (lane & 3);
+    const int vg = lane >> 4;
+    const int kpid = page_of(pr, i, kg);
+    const int vpid = page_of(pr, i, vg);
+    kp = row_ptr(p.k_cache, kpid, g, p.num_kv_heads, pr.log2ps, (base_tok + ktok) & ps_mask, G_::ROW) +
+         (lane >> 4) * G_::KQ;
+    vp = row_ptr(p.v_cache, vpid, g, p.num_kv_heads, pr.log2ps, (base_tok + 16 * vg) & ps_mask, G_::ROW) +
+         (lane & 15) * (G_::VW * 4);
+  } else {
+    const int ts = lane >> 3;
+    const int pid = page_of(pr, i, ts >> 1);
+    const int off = (lane & 7) * (G_::CW * 4);
+    kp = row_ptr(p.k_cache, pid, g, p.num_kv_heads, pr.log2ps, (base_tok + 8 * ts) & ps_mask, G_::ROW) + off;
+    vp = row_ptr(p.v_cache, pid, g, p.num_kv_heads, pr.log2ps, (base_tok + 8 * ts) & ps_mask, G_::ROW) + off;
+  }
+}
+
+template <int KV, int D, int GM, bool MFMA>
+__device__ __forceinline__ void load_tile(typename WaveState<KV, D, GM, MFMA>::Tile& t, const uint8_t* kp,
+                                          const uint8_t* vp) {
+  if constexpr (MFMA) {
+    mfma_load_k<KV, D>(t, kp);
+    mfma_load_v<KV, D>(t, vp);
+  } else {
+    valu_load<KV, D>(t, kp, vp);
+  }
+}
+
+template <int KV, int D, int GM, bool MFMA>
+__device__ __forceinline__ void compute_tile(typename WaveState<KV, D, GM, MFMA>::Tile& t,
+                                             typename WaveState<KV, D, GM, MFMA>::T& st, int valid,
+                                             float scale_log2, int lane) {
+  if constexpr (MFMA) {
+    f32x4_t s[4];
+    mfma_qk<KV, D>(t, st, s);
+    mfma_softmax_pv<KV, D>(t, st, s, valid, scale_log2, lane);
+  } else {
+    float s[8][GM];
+    valu_qk<KV, D, GM>(t, st, s);
+    valu_softmax_pv<KV, D, GM>(t, st, s, valid, scale_log2, lane);
+  }
+}
+
+template <int KV, int D, int GM, bool MFMA>
+__device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g, int L, int first_tile,
+                                             int n_wave_tiles, typename WaveState<KV, D, GM, MFMA>::T& st,
+                                             int lane) {
+  using Tile = typename WaveState<KV, D, GM, MFMA>::Tile;
+  const int log2ps = p.log2_page_size;
+  const int ppt_log2 = log2ps < 6 ? 6 - log2ps : 0;
+  const int round_tiles = 64 >> ppt_log2;
+  const int n_pages_b = (L + (1 << log2ps) - 1) >> log2ps;
+  const int64_t pt_row = (int64_t)b * p.max_pages;
+  const bool tags_on = p.page_tags != nullptr;
+  uint32_t status = 0;
+
+  for (int r0 = 0; r0 < n_wave_tiles; r0 += round_tiles) {
+    const int rt = min(round_tiles, n_wave_tiles - r0);
+    // lane j -> wave page j of this round
+    const int jt = lane >> ppt_log2;
+    const int tile_j = first_tile + 4 * (r0 + jt);
+    const int lp = log2ps < 6 ? (tile_j << ppt_log2) + (lane & ((1 << ppt_log2) - 1)) : (tile_j << 6) >> log2ps;
+    const bool used = jt < rt && lp < n_pages_b;
+    int pid = used ? p.page_table[pt_row + lp] : 0;
+    const bool bad = used && (pid < 0 || pid >= p.num_pages);
+    uint32_t expected = 0;
+    if (tags_on && used) expected = p.expected_tags[pt_row + lp];
+    uint32_t actual = expected;
+    if (tags_on && used && !bad) actual = p.page_tags[pid];
+    const bool any_bad = __any(bad);
+
+    PageRound pr;
+    pr.log2ps = log2ps;
+    pr.ppt_log2 = ppt_log2;
+    // Slots past the sequence's last page (only in its last tile) borrow the
+    // tile's first page, which always exists; their rows are masked.
+    const int first_pid = __shfl(pid, lane & ~((1 << ppt_log2) - 1));
+    pr.pid = (used && !bad) ? pid : first_pid;
+
+    const bool go = status == 0 && !any_bad;
+    Tile ta, tb;
+    const uint8_t *kp, *vp;
+    if (go) {
+      // Speculative: page ids are range-checked; data is not used before the tag ballot.
+      tile_pointers<KV, D, GM, MFMA>(p, pr, 0, first_tile + 4 * r0, g, lane, kp, vp);
+      load_tile<KV, D, GM, MFMA>(ta, kp, vp);
+    }
+    const bool any_mismatch = __any(actual != expected);
+    status |= (any_bad ? kAbortMeta : 0u) | (any_mismatch ? kAbortTag : 0u);
+    if (status != 0) continue;  // keep checking later rounds; compute nothing
+
+    const float sl = p.qk_scale_log2;
+    for (int i = 0; i < rt;) {
+      const int t0 = first_tile + 4 * (r0 + i);
+      if (i + 1 < rt) {
+        tile_pointers<KV, D, GM, MFMA>(p, pr, i + 1, t0 + 4, g, lane, kp, vp);
+        load_tile<KV, D, GM, MFMA>(tb, kp, vp);
+      }
+      compute_tile<KV, D, GM, MFMA>(ta, st, min(L - (t0 << 6), kTileTokens), sl, lane);
+      if (++i >= rt) break;
+      const int t1 = t0 + 4;
+      if (i + 1 < rt) {
+        tile_pointers<KV, D, GM, MFMA>(p, pr, i + 1, t1 + 4, g, lane, kp, vp);
+        load_tile<KV, D, GM, MFMA>(ta, kp, vp);
+      }
+      compute_tile<KV, D, GM, MFMA>(tb, st, min(L - (t1 << 6), kTileTokens), sl, lane);
+      ++i;
+    }
+  }
+  return status;
+}
+
+// ------------------------------------------------------------------------
+// Wave state -> LDS in the common layout m[w][h], l[w][h], acc[w][h][d].
+// ------------------------------------------------------------------------
+template <int KV, int D>
+__device__ __forceinline__ void export_state(MfmaState<KV, D>& st, MergeLds<D>& lds, int wave, int lane, int G) {
+  using G_ = Geo<KV, D>;
+  float l = xor_sum(st.l, 16);
+  l = xor_sum(l, 32);
+  const int h = lane & 15;
+  if (h < G) {
+#pragma unroll
+    for (int nb = 0; nb < G_::NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lds.acc[wave][h][G_::NB * (4 * (lane >> 4) + r) + nb] = st.acc[nb][r];
+    if (lane < 16) {
+      lds.m[wave][h] = st.m;
+      lds.l[wave][h] = l;
+    }
+  }
+}
+
+template <int KV, int D, int GM>
+__device__ __forceinline__ void export_state(ValuState<KV, D, GM>& st, MergeLds<D>& lds, int wave, int lane,
+                                             int G) {
+  constexpr int DC = Geo<KV, D>::DC;
+#pragma unroll
+  for (int h = 0; h < GM; ++h) {
+    float M = xor_max(st.m[h], 8);
+    M = xor_max(M, 16);
+    M = xor_max(M, 32);
+    const float w = st.m[h] == kNegInf ? 0.f : fast_exp2(st.m[h] - M);
+    float l = st.l[h] * w;
+    l = xor_sum(l, 8);
+    l = xor_sum(l, 16);
+    l = xor_sum(l, 32);
+#pragma unroll
+    for (int i = 0; i < DC; ++i) {
+      float a = st.acc[h][i] * w;
+      a = xor_sum(a, 8);
+      a = xor_sum(a, 16);
+      a = xor_sum(a, 32);
+      if (lane < 8 && h < G) lds.acc[wave][h][(lane & 7) * DC + i] = a;
+    }
+    if (lane == 0 && h < G) {
+      lds.m[wave][h] = M;
+      lds.l[wave][h] = l;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// The kernel.
+// ------------------------------------------------------------------------
+template <int KV, int D, int GM, bool MFMA>
+__global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
+  __shared__ MergeLds<D> lds;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.group;
+  const int L = p.seq_lens[b];
+  const bool meta_ok = L >= 1 && L <= (p.max_pages << p.log2_page_size);
+  const int n_tiles = meta_ok ? (L + kTileTokens - 1) / kTileTokens : 0;
+  const int n_splits = meta_ok ? (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split : 1;
+  if (split >= n_splits) return;
+  if (!meta_ok) {
+    if (tid == 0) p.abort_flags[b] = (uint8_t)kAbortMeta;
+    return;
+  }
+  const int tile_begin = split * p.tiles_per_split;
+  const int tile_count = min(p.tiles_per_split, n_tiles - tile_begin);
+  const int n_wave_tiles = tile_count > wave ? (tile_count - wave + kWavesPerBlock - 1) / kWavesPerBlock : 0;
+
+  // ---- this wave's query operand and initial state
+  typename WaveState<KV, D, GM, MFMA>::T st;
+  const uint16_t* qrow0 = p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
+  if constexpr (MFMA) {
+    using G_ = Geo<KV, D>;
+    const int col = lane & 15;
+    const int quarter = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < G_::KSTEPS; ++kk) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (col < G) w = *reinterpret_cast<const u32x4_t*>(qrow0 + (int64_t)col * D + quarter * (D / 4) + 8 * kk);
+      st.q[kk] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    st.m = kNegInf;
+    st.l = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < G_::NB; ++nb) st.acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  } else {
+    constexpr int DC = Geo<KV, D>::DC;
+    const int dc = lane & 7;
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      uint32_t w[DC / 2];
+      if (h < G) {
+        load_words<DC / 2>(reinterpret_cast<const uint8_t*>(qrow0 + (int64_t)h * D + dc * DC), w);
+      } else {
+#pragma unroll
+        for (int i = 0; i < DC / 2; ++i) w[i] = 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < DC / 2; ++i) st.q2[h][i] = w[i];
+      st.m[h] = kNegInf;
+      st.l[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < DC; ++i) st.acc[h][i] = 0.f;
+    }
+  }
+
+  const uint32_t wave_status =
+      run_wave<KV, D, GM, MFMA>(p, b, g, L, tile_begin + wave, n_wave_tiles, st, lane);
+  export_state(st, lds, wave, lane, G);
+  if (lane == 0) lds.status[wave] = wave_status;
+  __syncthreads();
+
+  uint32_t status = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) status |= lds.status[w];
+
+  const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
+  const float v_scale = p.v_scale;
+
+  if (n_splits == 1) {
+    // Only block of this (sequence, KV head): finish here.
+    if (tid == 0) p.abort_flags[b] = (uint8_t)status;
+    if (status != 0) return;
+    for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
+      const int h = e / D, d = e - h * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) M = __builtin_fmaxf(M, lds.m[w][h]);
+      float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float wt = lds.m[w][h] == kNegInf ? 0.f : fast_exp2(lds.m[w][h] - M);
+        Ls += lds.l[w][h] * wt;
+        a0 += lds.acc[w][h][d] * wt;
+        a1 += lds.acc[w][h][d + 1] * wt;
+      }
+      const float inv = v_scale / Ls;
+      const uint32_t packed = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
+      *reinterpret_cast<uint32_t*>(p.out + out_row0 + e) = packed;
+    }
+    return;
+  }
+
+  // ---- several splits: publish this block's partial
+  const int64_t pair = (int64_t)b * p.num_kv_heads + g;
+  const int64_t slot = pair * p.splits + split;
+  if (status == 0) {
+    for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
+      const int h = e / D, d = e - h * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) M = __builtin_fmaxf(M, lds.m[w][h]);
+      float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const float wt = lds.m[w][h] == kNegInf ? 0.f : fast_exp2(lds.m[w][h] - M);
+        Ls += lds.l[w][h] * wt;
+        a0 += lds.acc[w][h][d] * wt;
+        a1 += lds.acc[w][h][d + 1] * wt;
+      }
+      f32x2_t av = {a0, a1};
+      *reinterpret_cast<f32x2_t*>(p.split_acc + (slot * G + h) * D + d) = av;
+      if (d == 0) {
+        f32x2_t ml = {M, Ls};
+        *reinterpret_cast<f32x2_t*>(p.split_ml + (slot * G + h) * 2) = ml;
+      }
+    }
+  }
+  if (tid == 0) p.split_status[slot] = status;
+
+  // Release this block's partial to the whole device, then count arrivals.
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const uint32_t prev = __hip_atomic_fetch_add(p.counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds.flag = prev == (uint32_t)(n_splits - 1);
+  }
+  __syncthreads();
+  if (!lds.flag) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+
+  // ---- last arrival: merge all splits of this (sequence, KV head)
+  const int64_t slot0 = pair * p.splits;
+  uint32_t st_all = 0;
+  for (int s = tid; s < n_splits; s += kBlockThreads) st_all |= p.split_status[slot0 + s];
+  st_all = __ballot(st_all != 0) ? 1u : 0u;
+  if (lane == 0) lds.status[wave] = st_all;
+  __syncthreads();
+  bool aborted = false;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) aborted |= lds.status[w] != 0;
+  if (aborted) {
+    // Recover the exact bits (rare path).
+    if (tid == 0) {
+      uint32_t bits = 0;
+      for (int s = 0; s < n_splits; ++s) bits |= p.split_status[slot0 + s];
+      p.abort_flags[b] = (uint8_t)bits;
+      p.counters[pair] = 0u;
+    }
+    return;
+  }
+  if (tid == 0) {
+    p.abort_flags[b] = 0;
+    p.counters[pair] = 0u;
+  }
+  // weights per (split, head): w = exp2(m_s - M_h)
+  for (int e = tid; e < n_splits * G; e += kBlockThreads) {
+    const int s = e / G, h = e - s * G;
+    lds.w[s][h] = p.split_ml[((slot0 + s) * G + h) * 2];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = kNegInf;
+    for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, lds.w[s][tid]);
+    float Ls = 0.f;
+    for (int s = 0; s < n_splits; ++s) Ls += p.split_ml[((slot0 + s) * G + tid) * 2 + 1] * fast_exp2(lds.w[s][tid] - M);
+    lds.head_m[tid] = M;
+    lds.head_inv_l[tid] = v_scale / Ls;
+  }
+  __syncthreads();
+  for (int e = tid; e < n_splits * G; e += kBlockThreads) {
+    const int s = e / G, h = e - s * G;
+    lds.w[s][h] = fast_exp2(lds.w[s][h] - lds.head_m[h]);
+  }
+  __syncthreads();
+  for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
+    const int h = e / D, d = e - h * D;
+    float a0 = 0.f, a1 = 0.f;
+    for (int s = 0; s < n_splits; ++s) {
+      const f32x2_t av = *reinterpret_cast<const f32x2_t*>(p.split_acc + ((slot0 + s) * G + h) * D + d);
+      const float wt = lds.w[s][h];
+      a0 += av[0] * wt;
+      a1 += av[1] * wt;
+    }
+    const float inv = lds.head_inv_l[h];
+    const uint32_t packed = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
+    *reinterpret_cast<uint32_t*>(p.out + out_row0 + e) = packed;
+  }
+}
+
+template <int KV, int D, int GM, bool MFMA>
+hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
+  dim3 grid(p.splits, p.num_kv_heads, p.batch);
+  hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), grid, dim3(kBlockThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int KV, int D>
+hipError_t launch_dtype_dim(const DecodeParams& p, bool mfma, hipStream_t stream) {
+  if (mfma) return launch_one<KV, D, 16, true>(p, stream);
+  if (p.group <= 1) return launch_one<KV, D, 1, false>(p, stream);
+  if (p.group <= 2) return launch_one<KV, D, 2, false>(p, stream);
+  return launch_one<KV, D, 4, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma, hipStream_t stream) {
+  if (kv_dtype == 0) {
+    if (head_dim == 64) return launch_dtype_dim<0, 64>(p, mfma, stream);
+    return launch_dtype_dim<0, 128>(p, mfma, stream);
+  }
+  if (head_dim == 64) return launch_dtype_dim<1, 64>(p, mfma, stream);
+  return launch_dtype_dim<1, 128>(p, mfma, stream);
+}
+
+}  // namespace fp8kv

@@ -1,0 +1,67 @@
+// Internal interface between the C-ABI entry points (api.cpp) and the kernel
+// translation units.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fp8kv {
+
+constexpr int kTileTokens = 64;   // tokens per tile handled by one wave at a time
+constexpr int kWavesPerBlock = 4; // waves per workgroup; they split one chunk of tiles
+constexpr int kBlockThreads = 64 * kWavesPerBlock;
+constexpr int kMaxGroup = 16;     // query heads per KV head handled by one workgroup
+
+struct AppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* row_seq;
+  const int32_t* row_pos;
+  const int32_t* page_table;
+  void* k_cache;
+  void* v_cache;
+  float k_scale, v_scale;
+  int32_t batch, max_pages, num_pages, n_rows, num_kv_heads, head_dim, log2_page_size;
+};
+
+struct DecodeParams {
+  const uint16_t* q;                // bf16 [B][Hq][D]
+  const uint8_t* k_cache;           // [P][Hkv][PS][D] elements
+  const uint8_t* v_cache;
+  const int32_t* page_table;        // [B][max_pages]
+  const int32_t* seq_lens;          // [B]
+  const uint32_t* page_tags;        // [P] or null (check off)
+  const uint32_t* expected_tags;    // [B][max_pages] or null
+  uint16_t* out;                    // bf16 [B][Hq][D]
+  uint8_t* abort_flags;             // [B]
+  uint32_t* counters;               // [B*Hkv]   arrivals per (sequence, KV head)
+  uint32_t* split_status;           // [B*Hkv*S] abort bits seen by each split
+  float* split_ml;                  // [B*Hkv*S][G][2]  running max (log2 domain), sum
+  float* split_acc;                 // [B*Hkv*S][G][D]  unnormalized output
+  int32_t batch, num_q_heads, num_kv_heads, group, max_pages, num_pages;
+  int32_t log2_page_size;
+  int32_t tiles_per_split, splits;  // S = splits (per sequence, maximum)
+  float qk_scale_log2;              // softmax_scale * k_scale * log2(e)
+  float v_scale;                    // folded into the final normalization
+};
+
+// Work decomposition chosen on the host from sizes only (no device reads).
+struct SplitPlan {
+  int32_t tiles_per_split;
+  int32_t splits;
+};
+SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages,
+                      int32_t num_splits);
+
+struct WorkspaceLayout {
+  size_t counters, split_status, split_ml, split_acc, total;
+};
+WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t splits);
+
+hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,
+                         hipStream_t stream);
+
+}  // namespace fp8kv

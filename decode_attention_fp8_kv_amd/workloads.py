@@ -319,3 +319,39 @@ def kv_bytes(w: Workload, kv_dtype: int, flags=None) -> int:
         total += 2 * w.num_q_heads * w.head_dim * 2
         total += (-(-L // w.page_size)) * 12
     return total + w.batch
+
+
+def make_custom(lengths, num_q_heads, num_kv_heads, head_dim, page_size, *, num_pages=None, seed=0,
+                dist="normal", device="cpu", mismatch=(), spare_pages=3, softmax_scale=None,
+                q_scale=1.0) -> Workload:
+    """A small workload of any supported shape, for parity tests.
+
+    ``lengths`` are the tokens attended per sequence (all already cached);
+    the pool gets ``spare_pages`` unused pages beyond those needed (or exactly
+    ``num_pages``); ``mismatch`` lists (sequence, page slot) pairs whose
+    expected tag is flipped; ``dist`` is "normal" or "t3".
+    """
+    lengths = np.asarray(lengths, dtype=np.int64)
+    B = len(lengths)
+    need = int(sum(-(-int(L) // page_size) for L in lengths))
+    num_pages = need + spare_pages if num_pages is None else num_pages
+    dev = torch.device(device)
+    table, max_pages, n_used = _page_layout(np.maximum(lengths, 1), page_size, num_pages, seed)
+    tags, expected = _tags(table, n_used, num_pages, seed)
+    for b, j in mismatch:
+        expected[b, j] ^= np.uint32(1)
+    ctx_k, ctx_seq, ctx_pos = _rows(lengths, num_kv_heads, head_dim, dist, seed, 10, dev)
+    ctx_v, _, _ = _rows(lengths, num_kv_heads, head_dim, dist, seed, 11, dev)
+    k_scale, v_scale = _amax_scale(ctx_k), _amax_scale(ctx_v)
+    gq = _gen(dev.type, seed, 14)
+    q = (_normal((B, num_q_heads, head_dim), gq, dev) * q_scale).to(torch.bfloat16)
+    sm = 1.0 / math.sqrt(head_dim) if softmax_scale is None else softmax_scale
+    empty = torch.empty((0, num_kv_heads, head_dim), dtype=torch.bfloat16, device=dev)
+    none = torch.empty(0, dtype=torch.int32, device=dev)
+    return Workload(
+        name="custom", batch=B, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim=head_dim,
+        page_size=page_size, num_pages=num_pages, max_pages=max_pages,
+        seq_lens=lengths.astype(np.int32), page_table=table, page_tags=tags, expected_tags=expected,
+        softmax_scale=float(np.float32(sm)), k_scale=k_scale, v_scale=v_scale, q=q,
+        ctx_k=ctx_k, ctx_v=ctx_v, ctx_seq=ctx_seq, ctx_pos=ctx_pos,
+        new_k=empty, new_v=empty.clone(), new_seq=none, new_pos=none.clone(), seed=seed)

@@ -1,0 +1,201 @@
+/*
+ * fp8kv.h -- C ABI of the MI355X (gfx950) paged decode-attention library
+ * over an FP8 e4m3 KV cache with per-page generation tags.
+ *
+ * The method: a decode step's attention reads a paged KV cache that is held
+ * as 8-bit e4m3 floating point instead of BF16, which halves its size, and
+ * converts values as it reads them (page "Cloudflare tối ưu hóa Kimi và GLM
+ * trên Workers AI", section "Lượng tử hóa KV cache"; page "更小、更快、更安全
+ * ：大规模运行Kimi和GLM", section "量化 KV 缓存").  Every cache page of the
+ * shared pool carries a tag that changes on each reallocation; the tag is
+ * compared before the page is read and a mismatch aborts the request rather
+ * than returning wrong data; the check is optional (page "ترفندهای کلادفلر
+ * برای جا دادن مدل‌های غول‌پیکر تو GPU", third technique; page "Tối ưu hóa
+ * mô hình AI quy mô lớn", section "Bảo vệ tính toàn vẹn của KV Cache").  The
+ * e4m3 bit layout is the OCP OFP8 E4M3 encoding (bias 7, no infinities,
+ * NaN = S.1111.111, largest finite magnitude 448).
+ *
+ * Conventions for every call below
+ * --------------------------------
+ *  - Pointers are DEVICE pointers (memory on the current HIP device) unless
+ *    stated otherwise; the caller owns all memory, including the workspace.
+ *  - BF16 tensors are passed as uint16_t bit patterns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls are asynchronous on that stream: they enqueue kernels and return.
+ *    They never allocate memory, never synchronize and never read device
+ *    memory from the host.
+ *  - Argument checking happens on the host before anything is launched; a
+ *    negative status means nothing was launched and no memory was touched.
+ *  - Conditions found in device data (stale tags, bad page ids, bad lengths)
+ *    are results, not errors: they are reported in `abort_flags`.
+ *  - Calls are reentrant; different streams may run calls concurrently as
+ *    long as they do not share output or workspace buffers.
+ */
+#ifndef FP8KV_H
+#define FP8KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP8KV_ABI_VERSION 1
+
+/* KV cache element types. */
+#define FP8KV_KV_FP8_E4M3 0 /* 1 byte per element, value = e4m3(code) * scale */
+#define FP8KV_KV_BF16 1     /* 2 bytes per element, raw BF16, no scale       */
+
+/* Status codes (return values). */
+#define FP8KV_OK 0
+#define FP8KV_ERR_NULL (-1)        /* a required pointer is NULL                      */
+#define FP8KV_ERR_SHAPE (-2)       /* a size is <= 0, or heads do not divide          */
+#define FP8KV_ERR_UNSUPPORTED (-3) /* head_dim / page_size / group / dtype not built  */
+#define FP8KV_ERR_WORKSPACE (-4)   /* workspace smaller than the size function says   */
+#define FP8KV_ERR_SCALE (-5)       /* a scale is not finite or not > 0                */
+#define FP8KV_ERR_TAGS (-6)        /* exactly one of page_tags / expected_tags given  */
+#define FP8KV_ERR_LAUNCH (-7)      /* the HIP runtime rejected a launch               */
+#define FP8KV_ERR_ALIGN (-8)       /* q/k_new/v_new/caches not 16-byte aligned, out not
+                                      4-byte aligned, or workspace not 256-byte aligned */
+
+/* Abort-flag bits written per sequence by paged_decode_attn. */
+#define FP8KV_ABORT_TAG_MISMATCH 1u /* a used page's tag differs from the expected one */
+#define FP8KV_ABORT_BAD_METADATA 2u /* seq_len outside [1, max_pages*page_size], or a
+                                       used page id outside [0, num_pages)            */
+
+/* Supported shapes of this build. */
+#define FP8KV_MAX_GROUP 16 /* num_q_heads / num_kv_heads                      */
+/* head_dim in {64, 128}; page_size a power of two in [16, 256].               */
+
+/* ABI version of the loaded library (FP8KV_ABI_VERSION it was built with). */
+int fp8kv_abi_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fp8kv_status_string(int status);
+
+/* Text of the last HIP runtime error seen by this thread ("" if none). */
+const char* fp8kv_last_hip_error(void);
+
+/*
+ * kv_quant_append -- write new K/V rows into the paged caches.
+ *
+ * Row r (of n_rows) belongs to sequence row_seq[r] at token position
+ * row_pos[r]; it is written to physical page
+ *     page = page_table[row_seq[r] * max_pages + row_pos[r] / page_size]
+ * at slot row_pos[r] % page_size, for every KV head h and element d:
+ *     cache[((page * num_kv_heads + h) * page_size + slot) * head_dim + d].
+ *
+ * kv_dtype FP8KV_KV_FP8_E4M3: each element x becomes the e4m3 code of the
+ *   fp32 quotient fp32(x) / scale (an IEEE, correctly rounded fp32 division),
+ *   rounded to the nearest e4m3 value with ties to the even code, saturating
+ *   at +-448 (+-inf too); every NaN becomes 0x7F; K uses
+ *   k_scale and V uses v_scale (one fp32 scale per tensor).  Dequantized
+ *   values are code * scale.
+ * kv_dtype FP8KV_KV_BF16: the BF16 bits are copied; the scales are ignored.
+ *
+ *   k_new, v_new   uint16 BF16 [n_rows][num_kv_heads][head_dim]
+ *   row_seq        int32 [n_rows]   sequence index of each row
+ *   row_pos        int32 [n_rows]   token position of each row
+ *   page_table     int32 [batch][max_pages]
+ *   k_cache,
+ *   v_cache        [num_pages][num_kv_heads][page_size][head_dim] of
+ *                  uint8 (FP8) or uint16 (BF16)
+ *   k_scale,
+ *   v_scale        HOST fp32 values, finite and > 0 (FP8 mode only)
+ *
+ * A row whose sequence index is outside [0, batch), whose position is
+ * outside [0, max_pages*page_size) or whose page id is outside
+ * [0, num_pages) is skipped: nothing is ever written outside the pools.
+ * Rows aimed at the same slot are a caller error (the winner is unspecified).
+ * n_rows == 0 is valid and launches nothing.
+ */
+int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new,
+                    const int32_t* row_seq, const int32_t* row_pos,
+                    const int32_t* page_table, int32_t batch, int32_t max_pages,
+                    float k_scale, float v_scale,
+                    void* k_cache, void* v_cache, int32_t num_pages,
+                    int32_t n_rows, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t page_size, int32_t kv_dtype, void* stream);
+
+/*
+ * paged_decode_attn_workspace_size -- bytes of device workspace that
+ * paged_decode_attn needs for these sizes (0 never; always a multiple of 256).
+ * num_splits has the meaning it has in paged_decode_attn.  Returns 0 if the
+ * sizes are invalid.
+ */
+size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t page_size, int32_t max_pages,
+                                        int32_t num_splits);
+
+/*
+ * paged_decode_attn -- one decode step of attention for a batch of
+ * sequences, one query token each, over a paged FP8 (or BF16) KV cache.
+ *
+ * For sequence b with L = seq_lens[b] cached tokens and query head h
+ * (group size G = num_q_heads / num_kv_heads, KV head g = h / G):
+ *   k_t  = dequantized K row of token t (t < L) of KV head g,
+ *   s_t  = softmax_scale * <q[b][h], k_t>,
+ *   out[b][h] = sum_t softmax(s)_t * v_t     (rounded to BF16, nearest-even),
+ * where token t lives in page page_table[b*max_pages + t/page_size], slot
+ * t % page_size.  FP8 values are code * k_scale (K) and code * v_scale (V);
+ * BF16 values are used as stored and the scales are ignored.
+ *
+ *   q              uint16 BF16 [batch][num_q_heads][head_dim]
+ *   k_cache,
+ *   v_cache        [num_pages][num_kv_heads][page_size][head_dim]
+ *   page_table     int32 [batch][max_pages]; entries past the used pages
+ *                  are never read
+ *   seq_lens       int32 [batch]
+ *   page_tags      uint32 [num_pages]              current page generations
+ *   expected_tags  uint32 [batch][max_pages]       generations each sequence
+ *                  recorded; both NULL = tag check off (the default), both
+ *                  non-NULL = on, one NULL = FP8KV_ERR_TAGS
+ *   out            uint16 BF16 [batch][num_q_heads][head_dim]
+ *   abort_flags    uint8 [batch]; always written: 0, or an OR of the
+ *                  FP8KV_ABORT_* bits
+ *   workspace      device buffer of at least
+ *                  paged_decode_attn_workspace_size(...) bytes, 256-byte
+ *                  aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call
+ *                  leaves its counters at zero again, so it can be reused
+ *                  without clearing.  Calls sharing a workspace must be
+ *                  ordered (same stream).
+ *   num_splits     0 = choose automatically; n > 0 = split each sequence's
+ *                  tokens into about n contiguous ranges (flash-decoding),
+ *                  clamped to what the length allows.
+ *
+ * Tag rule: for every page slot j < ceil(L / page_size) (the partial last
+ * page included), the page id p = page_table[b*max_pages + j] must lie in
+ * [0, num_pages) (else bit FP8KV_ABORT_BAD_METADATA) and, when tags are on,
+ * page_tags[p] must equal expected_tags[b*max_pages + j] (else bit
+ * FP8KV_ABORT_TAG_MISMATCH).  Pages are checked before their contents are
+ * used.  When abort_flags[b] != 0, out[b] is NOT WRITTEN (left as it was).
+ * The caches are never written.  out must not alias q.
+ */
+int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache,
+                      int32_t kv_dtype, float k_scale, float v_scale,
+                      const int32_t* page_table, int32_t max_pages,
+                      const int32_t* seq_lens,
+                      const uint32_t* page_tags, const uint32_t* expected_tags,
+                      uint16_t* out, uint8_t* abort_flags,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                      float softmax_scale, int32_t num_splits, void* stream);
+
+/*
+ * paged_decode_attn_path -- which kernel family paged_decode_attn uses for a
+ * GQA group size: 1 = MFMA (groups of 5..16 query heads per KV head fill a
+ * 16-column matrix-core tile enough to be a dense contraction), 0 = VALU
+ * (groups of 1..4).  -1 for invalid sizes.  Setting FP8KV_FORCE_PATH=mfma
+ * (any group) or =valu (groups up to 4) in the environment overrides the
+ * choice, so tests can cross-check the two families on one shape.
+ */
+int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8KV_H */

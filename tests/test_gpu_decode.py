@@ -1,0 +1,181 @@
+"""paged_decode_attn on the GPU vs the oracle (small shapes that span several
+tiles, ragged tails, both kernel families, every supported page size).
+
+Each case: the same seeded inputs go to both sides; cache bytes and abort
+flags must match bit for bit; outputs within the stated tolerance; aborted
+sequences' outputs untouched.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import decode_attention_fp8_kv_amd as fk
+from decode_attention_fp8_kv_amd import workloads as W
+
+from parity import (OUT_SENTINEL, compare_outputs, gpu_decode, gpu_fill, oracle_decode, oracle_fill,
+                    pool_bits, say)
+
+pytestmark = pytest.mark.gpu
+
+FP8, BF16 = fk.KV_FP8_E4M3, fk.KV_BF16
+
+
+def _run_case(w, kv_dtype, dev, tags_on=True, num_splits=0, **over):
+    kc, vc = gpu_fill(w, kv_dtype, dev)
+    okc, ovc = oracle_fill(w, kv_dtype)
+    assert np.array_equal(pool_bits(kc), okc), "K cache bytes differ from the oracle"
+    assert np.array_equal(pool_bits(vc), ovc), "V cache bytes differ from the oracle"
+    out, flags, ws = gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=tags_on, num_splits=num_splits, **over)
+    ref, rflags = oracle_decode(w, kv_dtype, okc, ovc, tags_on=tags_on, **over)
+    assert np.array_equal(flags, rflags), f"abort flags {flags} != oracle {rflags}"
+    compare_outputs(out, ref, flags)
+    # every arrival counter is back at zero, ready for the next call
+    n_pairs = w.batch * w.num_kv_heads
+    assert int(ws[:4 * n_pairs].count_nonzero()) == 0
+    return out, flags, (kc, vc)
+
+
+def test_tiny_config_fp8_and_bf16(gpu_device):
+    for kv in (FP8, BF16):
+        say(f"tiny config kv={kv}")
+        w = W.make("tiny")
+        out, flags, _ = _run_case(w, kv, gpu_device)
+        assert flags.tolist() == [0, fk.ABORT_TAG_MISMATCH]
+        say(f"tiny config kv={kv} tags off")
+        out, flags, _ = _run_case(w, kv, gpu_device, tags_on=False)
+        assert flags.tolist() == [0, 0]
+
+
+SHAPES = [
+    # lengths, Hq, Hkv, D, PS
+    ([100, 257], 8, 2, 64, 16),              # tiny-like, VALU (G=4)
+    ([1, 15, 16, 17, 63, 64, 65], 8, 1, 128, 16),   # G=8 MFMA, every tail shape
+    ([300, 1000, 4097], 64, 8, 128, 64),      # main shape, several tiles
+    ([129, 700], 16, 1, 128, 32),             # G=16
+    ([333, 64, 1], 6, 1, 64, 128),            # G=6, padded columns
+    ([777, 50], 10, 2, 128, 256),             # G=5
+    ([500, 31], 2, 2, 128, 16),               # G=1 VALU
+    ([999, 65, 2], 4, 2, 64, 64),             # G=2 VALU
+    ([1200], 16, 4, 64, 16),                  # G=4 VALU, D=64
+]
+
+
+@pytest.mark.parametrize("kv_dtype", [FP8, BF16])
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[1]}x{s[2]}d{s[3]}ps{s[4]}" for s in SHAPES])
+def test_shapes(gpu_device, shape, kv_dtype):
+    lengths, hq, hkv, d, ps = shape
+    say(f"shape {shape} kv={kv_dtype}")
+    w = W.make_custom(lengths, hq, hkv, d, ps, seed=sum(lengths) + hq, mismatch=[])
+    _run_case(w, kv_dtype, gpu_device)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 32, 300])
+@pytest.mark.parametrize("hq,hkv", [(64, 8), (8, 2)])
+def test_split_counts(gpu_device, num_splits, hq, hkv):
+    say(f"splits={num_splits} hq={hq} hkv={hkv}")
+    w = W.make_custom([5000, 2100, 64, 1], hq, hkv, 128, 64, seed=num_splits)
+    _run_case(w, FP8, gpu_device, num_splits=num_splits)
+
+
+def test_deterministic_and_layout_invariant(gpu_device):
+    say("determinism + physical page permutation")
+    w1 = W.make_custom([3000, 129], 64, 8, 128, 16, seed=11)
+    w2 = W.make_custom([3000, 129], 64, 8, 128, 16, seed=11, spare_pages=40)   # other pool, other table
+    assert not np.array_equal(w1.page_table, w2.page_table) or w1.num_pages != w2.num_pages
+    a, _, _ = _run_case(w1, FP8, gpu_device)
+    b, _, _ = _run_case(w1, FP8, gpu_device)
+    assert np.array_equal(a, b), "two identical calls gave different bits"
+    c, _, _ = _run_case(w2, FP8, gpu_device)
+    assert np.array_equal(a, c), "outputs depend on where pages live"
+
+
+def test_tag_and_metadata_cases(gpu_device):
+    w = W.make_custom([200, 300, 64, 65, 500], 16, 2, 128, 16, seed=5, mismatch=[(0, 3), (1, 18), (3, 5)])
+    lens = w.seq_lens.copy()
+    # seq 0: mismatch in a full page; seq 1: in the partial last page (300 = 18*16 + 12);
+    # seq 3: mismatch only in slot 5, beyond its 5 used pages (65 tokens) -> no abort
+    pt = w.page_table.copy()
+    pt[4, 10] = w.num_pages + 3               # seq 4: page id out of range -> bit 1
+    lens[2] = 0                               # seq 2: empty -> bit 1
+    for kv in (FP8, BF16):
+        say(f"tag/metadata cases kv={kv}")
+        kc, vc = gpu_fill(w, kv, gpu_device)
+        okc, ovc = oracle_fill(w, kv)
+        out, flags, _ = gpu_decode(w, kv, kc, vc, gpu_device, seq_lens=lens, page_table=pt)
+        ref, rflags = oracle_decode(w, kv, okc, ovc, seq_lens=lens, page_table=pt)
+        assert rflags.tolist() == [1, 1, 2, 0, 2]
+        assert np.array_equal(flags, rflags)
+        compare_outputs(out, ref, flags)
+        # stale tag: bump a page's generation (reallocated) -> its owner aborts
+        tags = w.page_tags.copy()
+        tags[w.page_table[3, 0]] += np.uint32(1)
+        out, flags, _ = gpu_decode(w, kv, kc, vc, gpu_device, page_tags=tags)
+        ref, rflags = oracle_decode(w, kv, okc, ovc, page_tags=tags)
+        assert np.array_equal(flags, rflags) and flags[3] == 1
+        compare_outputs(out, ref, flags)
+        # tags off: only metadata problems abort
+        out, flags, _ = gpu_decode(w, kv, kc, vc, gpu_device, tags_on=False, seq_lens=lens, page_table=pt)
+        ref, rflags = oracle_decode(w, kv, okc, ovc, tags_on=False, seq_lens=lens, page_table=pt)
+        assert rflags.tolist() == [0, 0, 2, 0, 2] and np.array_equal(flags, rflags)
+        compare_outputs(out, ref, flags)
+
+
+@pytest.mark.parametrize("num_splits", [1, 5])
+def test_mismatch_in_every_split_position(gpu_device, num_splits):
+    # one stale page at a time, in each page slot of a long sequence
+    w = W.make_custom([1100, 90], 8, 1, 128, 64, seed=21)
+    kc, vc = gpu_fill(w, FP8, gpu_device)
+    okc, ovc = oracle_fill(w, FP8)
+    for j in range(0, 18):
+        say(f"stale page slot {j} splits={num_splits}")
+        exp = w.expected_tags.copy()
+        exp[0, j] ^= np.uint32(0x80000000)
+        out, flags, _ = gpu_decode(w, FP8, kc, vc, gpu_device, expected_tags=exp, num_splits=num_splits)
+        assert flags.tolist() == [1, 0]
+        assert np.all(out[0] == OUT_SENTINEL)
+        ref, rflags = oracle_decode(w, FP8, okc, ovc, expected_tags=exp)
+        compare_outputs(out, ref, flags)
+
+
+def test_valu_and_mfma_families_agree(gpu_device, monkeypatch):
+    w = W.make_custom([2000, 77, 640], 8, 2, 128, 32, seed=8)
+    outs = {}
+    for path in ("valu", "mfma"):
+        say(f"forced path {path}")
+        monkeypatch.setenv("FP8KV_FORCE_PATH", path)
+        assert fk.paged_decode_attn_path(8, 2) == (1 if path == "mfma" else 0)
+        outs[path], _, _ = _run_case(w, FP8, gpu_device)
+    from parity import bf16_bits_to_f64
+    a, e = bf16_bits_to_f64(outs["valu"]), bf16_bits_to_f64(outs["mfma"])
+    assert np.abs(a - e).max() <= 2e-2
+
+
+def test_equal_keys_give_mean_of_values_on_gpu(gpu_device):
+    # All K rows identical -> softmax is uniform -> output = mean of the V rows.
+    say("equal keys -> mean of V")
+    w = W.make_custom([1500, 333], 64, 8, 128, 64, seed=4)
+    k0 = w.ctx_k[:1].clone()
+    w.ctx_k = k0.expand_as(w.ctx_k).contiguous()
+    w.k_scale = float(np.float32(float(k0.float().abs().max()) / 448.0))
+    out, flags, _ = _run_case(w, FP8, gpu_device)
+    from parity import bf16_bits_to_f64, oracle_fill
+    from oracle import e4m3
+    okc, ovc = oracle_fill(w, FP8)
+    for b, L in enumerate(w.seq_lens):
+        pages = w.page_table[b]
+        t = np.arange(L)
+        v = e4m3.dequantize(ovc[pages[t // 64], :, t % 64, :], w.v_scale)   # [L][Hkv][D]
+        mean = v.mean(axis=0)
+        got = bf16_bits_to_f64(out[b]).reshape(8, 8, 128)
+        assert np.abs(got - mean[:, None, :]).max() <= 2e-2 + 2.0 ** -8 * np.abs(mean).max()
+
+
+def test_large_scores_and_tiny_values(gpu_device):
+    # Peaked softmax (large q) and a t-distributed cache: saturation and subnormal codes.
+    say("peaked softmax, t3 values")
+    w = W.make_custom([3000, 100], 64, 8, 128, 64, seed=13, dist="t3", q_scale=4.0)
+    _run_case(w, FP8, gpu_device)
+    _run_case(w, BF16, gpu_device)
