@@ -206,8 +206,8 @@ def main():
     ap.add_argument("--no-bf16", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        print("bench.py measures one GPU only: decode sequences shard across GPUs with no exchange "
+              "between them, and no multi-GPU run is made.", file=sys.stderr)
         sys.exit(2)
 
     import torch

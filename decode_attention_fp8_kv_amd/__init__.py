@@ -137,20 +137,20 @@ def kv_quant_append(k_new, v_new, row_seq, row_pos, page_table, k_scale, v_scale
 
 
 def paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages,
-                                     num_splits=0) -> int:
+                                     num_blocks=0) -> int:
     return int(load_library().paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
-                                                               page_size, max_pages, num_splits))
+                                                               page_size, max_pages, num_blocks))
 
 
 def paged_decode_attn_path(num_q_heads, num_kv_heads) -> int:
     return int(load_library().paged_decode_attn_path(num_q_heads, num_kv_heads))
 
 
-def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, num_splits=0,
+def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, num_blocks=0,
                     device="cuda"):
     """A zero-filled workspace of the size the library asks for (allocated by torch)."""
     n = paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages,
-                                         num_splits)
+                                         num_blocks)
     if n == 0:
         raise ValueError("invalid sizes for a workspace")
     return torch.zeros(n, dtype=torch.uint8, device=device)
@@ -158,7 +158,7 @@ def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_p
 
 def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flags, workspace, *,
                       kv_dtype=KV_FP8_E4M3, k_scale=1.0, v_scale=1.0, page_tags=None, expected_tags=None,
-                      softmax_scale=None, num_splits=0, stream=None):
+                      softmax_scale=None, num_blocks=0, stream=None):
     """One decode step of attention; writes ``out`` (bf16) and ``abort_flags`` (uint8).
 
     See ``paged_decode_attn`` in ``include/fp8kv.h`` for the exact semantics.
@@ -178,6 +178,6 @@ def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flag
         _ptr(page_tags, _U32, "page_tags", dev), _ptr(expected_tags, _U32, "expected_tags", dev),
         _ptr(out, _BF16, "out", dev), _ptr(abort_flags, (torch.uint8,), "abort_flags", dev),
         _ptr(workspace, (torch.uint8,), "workspace", dev), workspace.numel(),
-        batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_splits),
+        batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_blocks),
         _stream_handle(dev, stream))
     _check("paged_decode_attn", status)

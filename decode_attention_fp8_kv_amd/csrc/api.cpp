@@ -36,43 +36,40 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
-constexpr int64_t kTargetBlocks = 8192;  // enough blocks to keep 256 CUs busy through a ragged tail
-constexpr int kMaxSplits = 256;          // bound of the final merge's per-split weight table
+constexpr int64_t kResidentBlocks = 512;  // 2 blocks of 4 waves on each of MI355X's 256 CUs
+constexpr int64_t kMinTilesPerBlock = 16; // below this, fewer blocks: merge cost beats parallelism
+constexpr int64_t kMaxBlocks = 65535;
+constexpr int64_t kMaxTotalTiles = int64_t(1) << 40;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+int64_t max_total_tiles(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages) {
+  const int64_t max_tiles = ((int64_t)max_pages * page_size + kTileTokens - 1) / kTileTokens;
+  return (int64_t)batch * num_kv_heads * max_tiles;
+}
+
 }  // namespace
 
-SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages,
-                      int32_t num_splits) {
-  const int64_t max_tokens = (int64_t)max_pages * page_size;
-  const int64_t max_tiles = (max_tokens + kTileTokens - 1) / kTileTokens;
-  int64_t splits;
-  if (num_splits > 0) {
-    splits = num_splits;
-  } else {
-    const int64_t pairs = (int64_t)batch * num_kv_heads;
-    splits = (kTargetBlocks + pairs - 1) / pairs;
-    // keep at least one tile per wave in a split when the context allows
-    splits = std::min<int64_t>(splits, std::max<int64_t>(1, max_tiles / kWavesPerBlock));
+int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages, int32_t num_blocks) {
+  int64_t nb = num_blocks;
+  if (nb <= 0) {
+    const int64_t bound = max_total_tiles(batch, num_kv_heads, page_size, max_pages);
+    nb = std::min(kResidentBlocks, (bound + kMinTilesPerBlock - 1) / kMinTilesPerBlock);
   }
-  splits = std::max<int64_t>(1, std::min<int64_t>({splits, max_tiles, (int64_t)kMaxSplits}));
-  SplitPlan plan;
-  plan.tiles_per_split = (int32_t)((max_tiles + splits - 1) / splits);
-  plan.splits = (int32_t)((max_tiles + plan.tiles_per_split - 1) / plan.tiles_per_split);
-  return plan;
+  return (int32_t)std::max<int64_t>(1, std::min(nb, kMaxBlocks));
 }
 
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t splits) {
+                                 int32_t num_blocks) {
   const size_t pairs = (size_t)batch * num_kv_heads;
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
+  const size_t slots = 2 * (size_t)num_blocks;
   WorkspaceLayout w;
   w.counters = 0;
-  w.split_status = round_up(pairs * sizeof(uint32_t), 256);
-  w.split_ml = w.split_status + round_up(pairs * splits * sizeof(uint32_t), 256);
-  w.split_acc = w.split_ml + round_up(pairs * splits * group * 2 * sizeof(float), 256);
-  w.total = w.split_acc + round_up(pairs * splits * group * head_dim * sizeof(float), 256);
+  w.part_status = round_up(pairs * sizeof(uint32_t), 256);
+  w.part_ml = w.part_status + round_up(slots * sizeof(uint32_t), 256);
+  w.part_acc = w.part_ml + round_up(slots * group * 2 * sizeof(float), 256);
+  w.total = w.part_acc + round_up(slots * group * head_dim * sizeof(float), 256);
   return w;
 }
 
@@ -139,11 +136,11 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t*
 }
 
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                        int32_t page_size, int32_t max_pages, int32_t num_splits) {
-  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_splits < 0) return 0;
+                                        int32_t page_size, int32_t max_pages, int32_t num_blocks) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_blocks < 0) return 0;
   if (num_q_heads % num_kv_heads != 0 || !supported_head_dim(head_dim) || log2_page_size(page_size) < 0) return 0;
-  const SplitPlan plan = plan_splits(batch, num_kv_heads, page_size, max_pages, num_splits);
-  return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, plan.splits).total;
+  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks);
+  return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb).total;
 }
 
 int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads) {
@@ -159,9 +156,9 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       const uint32_t* page_tags, const uint32_t* expected_tags, uint16_t* out, uint8_t* abort_flags,
                       void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
-                      float softmax_scale, int32_t num_splits, void* stream) {
+                      float softmax_scale, int32_t num_blocks, void* stream) {
   if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_pages <= 0 || num_splits < 0)
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_pages <= 0 || num_blocks < 0)
     return FP8KV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return FP8KV_ERR_SHAPE;
   if (batch > 65535 || num_kv_heads > 65535) return FP8KV_ERR_SHAPE;
@@ -170,6 +167,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   const int l2ps = log2_page_size(page_size);
   if (l2ps < 0) return FP8KV_ERR_UNSUPPORTED;
   if ((int64_t)max_pages * page_size > INT32_MAX) return FP8KV_ERR_SHAPE;
+  if (max_total_tiles(batch, num_kv_heads, page_size, max_pages) > kMaxTotalTiles) return FP8KV_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !page_table || !seq_lens || !out || !abort_flags || !workspace)
     return FP8KV_ERR_NULL;
   if ((page_tags == nullptr) != (expected_tags == nullptr)) return FP8KV_ERR_TAGS;
@@ -179,8 +177,8 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   if (!aligned(q, 16) || !aligned(out, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(workspace, 256))
     return FP8KV_ERR_ALIGN;
-  const SplitPlan plan = plan_splits(batch, num_kv_heads, page_size, max_pages, num_splits);
-  const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, plan.splits);
+  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks);
+  const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb);
   if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;
 
   const double log2e = 1.4426950408889634;
@@ -196,9 +194,9 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   p.abort_flags = abort_flags;
   uint8_t* base = static_cast<uint8_t*>(workspace);
   p.counters = reinterpret_cast<uint32_t*>(base + ws.counters);
-  p.split_status = reinterpret_cast<uint32_t*>(base + ws.split_status);
-  p.split_ml = reinterpret_cast<float*>(base + ws.split_ml);
-  p.split_acc = reinterpret_cast<float*>(base + ws.split_acc);
+  p.part_status = reinterpret_cast<uint32_t*>(base + ws.part_status);
+  p.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
+  p.part_acc = reinterpret_cast<float*>(base + ws.part_acc);
   p.batch = batch;
   p.num_q_heads = num_q_heads;
   p.num_kv_heads = num_kv_heads;
@@ -206,8 +204,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   p.max_pages = max_pages;
   p.num_pages = num_pages;
   p.log2_page_size = l2ps;
-  p.tiles_per_split = plan.tiles_per_split;
-  p.splits = plan.splits;
+  p.num_blocks = nb;
   if (kv_dtype == FP8KV_KV_FP8_E4M3) {
     p.qk_scale_log2 = (float)((double)softmax_scale * (double)k_scale * log2e);
     p.v_scale = v_scale;

@@ -17,16 +17,19 @@
 //
 // Work decomposition
 // ------------------
-// grid = (splits, num_kv_heads, batch), 256 threads (4 waves) per block.
-// A block owns `tiles_per_split` consecutive 64-token tiles of one
-// (sequence, KV head); its 4 waves take every 4th tile and each keeps its
-// own online-softmax state (running max m, sum l, unnormalized acc).  The
-// waves merge through LDS; the block then either writes the output directly
-// (one split) or stores its partial (m, l, acc, status) in the workspace and
-// bumps an arrival counter -- the block that arrives last for its
-// (sequence, KV head) merges all partials (log-sum-exp) and writes the
-// output and the abort flag, then resets the counter to zero.
-//
+// The batch's work is the flattened list of (sequence, KV head, 64-token
+// tile) triples; a 1-D grid of num_blocks blocks of 256 threads (4 waves)
+// cuts it into equal contiguous shares (see "The balanced schedule" below),
+// so every block streams the same number of bytes whatever the length mix
+// and long sequences are split across blocks (flash-decoding).  Within a
+// piece of one (sequence, KV head), the 4 waves take every 4th tile and each
+// keeps its own online-softmax state (running max m, sum l, unnormalized
+// acc); the waves merge through LDS.  A piece that is a whole segment is
+// finished in place; a partial piece is stored in the workspace and the
+// block that arrives last for its (sequence, KV head) merges all partials
+// (log-sum-exp), writes the output and the abort flag, and resets the
+// arrival counter to zero.
+
 // Per wave and tile (MFMA family, group of 5..16 query heads per KV head):
 //   * K rows: lane l loads a quarter of one token's row (bytes of dims
 //     [q*D/4, (q+1)*D/4), q = l/16) for 4 token blocks; 16 lanes cover one
@@ -58,7 +61,7 @@ namespace {
 constexpr uint32_t kAbortTag = 1u;
 constexpr uint32_t kAbortMeta = 2u;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kMaxCombineSplits = 256;
+constexpr int kCombineChunk = 256;
 
 template <int D>
 struct MergeLds {
@@ -66,14 +69,14 @@ struct MergeLds {
   float l[kWavesPerBlock][kMaxGroup];
   union {
     float acc[kWavesPerBlock][kMaxGroup][D];
-    float w[kMaxCombineSplits][kMaxGroup];  // final combine: per-split weights
+    float w[kCombineChunk][kMaxGroup];  // final merge: weights of a chunk of partials
   };
   float head_m[kMaxGroup];
   float head_inv_l[kMaxGroup];
   uint32_t status[kWavesPerBlock];
   uint32_t flag;
 };
-static_assert(sizeof(float) * kWavesPerBlock * kMaxGroup * 64 >= sizeof(float) * kMaxCombineSplits * kMaxGroup,
+static_assert(sizeof(float) * kWavesPerBlock * kMaxGroup * 64 >= sizeof(float) * kCombineChunk * kMaxGroup,
               "combine weights must fit in the merge buffer");
 
 // ------------------------------------------------------------------------
@@ -570,26 +573,89 @@ __device__ __forceinline__ void export_state(ValuState<KV, D, GM>& st, MergeLds<
 }
 
 // ------------------------------------------------------------------------
-// The kernel.
+// The balanced schedule.
+//
+// All work of one call is the flattened list of (sequence b, KV head g,
+// tile t) triples, ordered b-major, then g, then t; sequence b contributes
+// num_kv_heads segments of T_b = ceil(L_b / 64) tiles (0 for a sequence
+// whose length is invalid).  Block k of nb takes the index range
+// [k*TT/nb, (k+1)*TT/nb) of the TT triples, so every block streams the same
+// number of tiles (+-1) whatever the length mix.  Each block derives the
+// schedule itself from seq_lens; the host never reads device memory.
+//
+// A block's range is cut into pieces, one per segment it touches.  A piece
+// that is a whole segment is finished in place.  Otherwise only the first
+// and the last piece of a block can be partial: the first is stored in the
+// block's partial slot 0 (it starts at the range start), the last in slot 1.
+// The block that arrives last for a segment (arrival counter per (b, g))
+// merges the partials of blocks block_of(seg_lo) .. block_of(seg_hi - 1).
 // ------------------------------------------------------------------------
-template <int KV, int D, int GM, bool MFMA>
-__global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
-  __shared__ MergeLds<D> lds;
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = p.group;
-  const int L = p.seq_lens[b];
-  const bool meta_ok = L >= 1 && L <= (p.max_pages << p.log2_page_size);
-  const int n_tiles = meta_ok ? (L + kTileTokens - 1) / kTileTokens : 0;
-  const int n_splits = meta_ok ? (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split : 1;
-  if (split >= n_splits) return;
-  if (!meta_ok) {
-    if (tid == 0) p.abort_flags[b] = (uint8_t)kAbortMeta;
-    return;
+__device__ __forceinline__ int64_t range_start(int64_t k, int64_t total, int64_t nb) { return k * total / nb; }
+// the block whose range holds flattened index x
+__device__ __forceinline__ int64_t block_of(int64_t x, int64_t total, int64_t nb) { return ((x + 1) * nb - 1) / total; }
+
+struct ScanLds {
+  int64_t v[kBlockThreads];
+  int32_t tiles[kBlockThreads];
+  int64_t excl[kBlockThreads];
+  int32_t lo, hi;
+};
+
+// Inclusive scan of one int64 per thread over the block (Hillis-Steele in
+// LDS); `total` receives the block-wide sum.
+__device__ __forceinline__ int64_t block_inclusive_scan(int64_t x, ScanLds& sl, int tid, int64_t& total) {
+  sl.v[tid] = x;
+  __syncthreads();
+#pragma unroll
+  for (int off = 1; off < kBlockThreads; off <<= 1) {
+    const int64_t t = tid >= off ? sl.v[tid - off] : 0;
+    __syncthreads();
+    sl.v[tid] += t;
+    __syncthreads();
   }
-  const int tile_begin = split * p.tiles_per_split;
-  const int tile_count = min(p.tiles_per_split, n_tiles - tile_begin);
-  const int n_wave_tiles = tile_count > wave ? (tile_count - wave + kWavesPerBlock - 1) / kWavesPerBlock : 0;
+  const int64_t r = sl.v[tid];
+  total = sl.v[kBlockThreads - 1];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ int seq_tiles(int L, int max_tokens) {
+  return (L >= 1 && L <= max_tokens) ? (L + kTileTokens - 1) / kTileTokens : 0;
+}
+
+// Merge the 4 waves' states of one (h, d-pair) element group.
+template <int D>
+__device__ __forceinline__ void merge_waves(const MergeLds<D>& lds, int h, int d, float& M, float& Ls, float& a0,
+                                            float& a1) {
+  M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) M = __builtin_fmaxf(M, lds.m[w][h]);
+  Ls = 0.f;
+  a0 = 0.f;
+  a1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWavesPerBlock; ++w) {
+    const float wt = lds.m[w][h] == kNegInf ? 0.f : fast_exp2(lds.m[w][h] - M);
+    Ls += lds.l[w][h] * wt;
+    a0 += lds.acc[w][h][d] * wt;
+    a1 += lds.acc[w][h][d + 1] * wt;
+  }
+}
+
+__device__ __forceinline__ void store_bf16_pair(uint16_t* dst, float a0, float a1) {
+  *reinterpret_cast<uint32_t*>(dst) = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
+}
+
+// One piece: tiles [t_lo, t_hi) of segment (b, g), whose flattened range is
+// [seg_lo, seg_lo + T).  Ends with a block barrier (LDS is reused next).
+template <int KV, int D, int GM, bool MFMA>
+__device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>& lds, int b, int g, int L, int T,
+                                              int t_lo, int t_hi, int64_t seg_lo, int64_t r0, int64_t TT,
+                                              int64_t nb, int k, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int G = p.group;
+  const int count = t_hi - t_lo;
+  const int n_wave_tiles = count > wave ? (count - wave + kWavesPerBlock - 1) / kWavesPerBlock : 0;
 
   // ---- this wave's query operand and initial state
   typename WaveState<KV, D, GM, MFMA>::T st;
@@ -607,7 +673,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
     st.m = kNegInf;
     st.l = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < G_::NB; ++nb) st.acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb_ = 0; nb_ < G_::NB; ++nb_) st.acc[nb_] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   } else {
     constexpr int DC = Geo<KV, D>::DC;
     const int dc = lane & 7;
@@ -629,8 +695,7 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
     }
   }
 
-  const uint32_t wave_status =
-      run_wave<KV, D, GM, MFMA>(p, b, g, L, tile_begin + wave, n_wave_tiles, st, lane);
+  const uint32_t wave_status = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo + wave, n_wave_tiles, st, lane);
   export_state(st, lds, wave, lane, G);
   if (lane == 0) lds.status[wave] = wave_status;
   __syncthreads();
@@ -638,135 +703,211 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
   uint32_t status = 0;
 #pragma unroll
   for (int w = 0; w < kWavesPerBlock; ++w) status |= lds.status[w];
-
   const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
   const float v_scale = p.v_scale;
 
-  if (n_splits == 1) {
-    // Only block of this (sequence, KV head): finish here.
+  if (t_lo == 0 && t_hi == T) {
+    // The whole segment is here: finish it.
     if (tid == 0) p.abort_flags[b] = (uint8_t)status;
-    if (status != 0) return;
-    for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
-      const int h = e / D, d = e - h * D;
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) M = __builtin_fmaxf(M, lds.m[w][h]);
-      float Ls = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) {
-        const float wt = lds.m[w][h] == kNegInf ? 0.f : fast_exp2(lds.m[w][h] - M);
-        Ls += lds.l[w][h] * wt;
-        a0 += lds.acc[w][h][d] * wt;
-        a1 += lds.acc[w][h][d + 1] * wt;
+    if (status == 0) {
+      for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
+        const int h = e / D, d = e - h * D;
+        float M, Ls, a0, a1;
+        merge_waves(lds, h, d, M, Ls, a0, a1);
+        const float inv = v_scale / Ls;
+        store_bf16_pair(p.out + out_row0 + e, a0 * inv, a1 * inv);
       }
-      const float inv = v_scale / Ls;
-      const uint32_t packed = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
-      *reinterpret_cast<uint32_t*>(p.out + out_row0 + e) = packed;
     }
+    __syncthreads();
     return;
   }
 
-  // ---- several splits: publish this block's partial
-  const int64_t pair = (int64_t)b * p.num_kv_heads + g;
-  const int64_t slot = pair * p.splits + split;
+  // ---- a partial piece: publish it
+  const int64_t slot = 2 * (int64_t)k + ((seg_lo + t_lo) == r0 ? 0 : 1);
   if (status == 0) {
     for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
       const int h = e / D, d = e - h * D;
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) M = __builtin_fmaxf(M, lds.m[w][h]);
-      float Ls = 0.f, a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) {
-        const float wt = lds.m[w][h] == kNegInf ? 0.f : fast_exp2(lds.m[w][h] - M);
-        Ls += lds.l[w][h] * wt;
-        a0 += lds.acc[w][h][d] * wt;
-        a1 += lds.acc[w][h][d + 1] * wt;
-      }
-      f32x2_t av = {a0, a1};
-      *reinterpret_cast<f32x2_t*>(p.split_acc + (slot * G + h) * D + d) = av;
-      if (d == 0) {
-        f32x2_t ml = {M, Ls};
-        *reinterpret_cast<f32x2_t*>(p.split_ml + (slot * G + h) * 2) = ml;
-      }
+      float M, Ls, a0, a1;
+      merge_waves(lds, h, d, M, Ls, a0, a1);
+      *reinterpret_cast<f32x2_t*>(p.part_acc + (slot * G + h) * D + d) = f32x2_t{a0, a1};
+      if (d == 0) *reinterpret_cast<f32x2_t*>(p.part_ml + (slot * G + h) * 2) = f32x2_t{M, Ls};
     }
   }
-  if (tid == 0) p.split_status[slot] = status;
+  if (tid == 0) p.part_status[slot] = status;
 
-  // Release this block's partial to the whole device, then count arrivals.
+  // Release the partial device-wide, then count arrivals for this segment.
+  const int64_t pair = (int64_t)b * p.num_kv_heads + g;
+  const int64_t first = block_of(seg_lo, TT, nb);
+  const int n_arr = (int)(block_of(seg_lo + T - 1, TT, nb) - first + 1);
   __syncthreads();
   if (tid == 0) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t prev = __hip_atomic_fetch_add(p.counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds.flag = prev == (uint32_t)(n_splits - 1);
+    lds.flag = prev == (uint32_t)(n_arr - 1);
   }
   __syncthreads();
   if (!lds.flag) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
-  // ---- last arrival: merge all splits of this (sequence, KV head)
-  const int64_t slot0 = pair * p.splits;
+  // ---- last arrival: merge the partials of blocks first .. first + n_arr - 1
+  const int64_t first_slot = 2 * first + (range_start(first, TT, nb) < seg_lo ? 1 : 0);
+  auto slot_of = [&](int a) -> int64_t { return a == 0 ? first_slot : 2 * (first + a); };
   uint32_t st_all = 0;
-  for (int s = tid; s < n_splits; s += kBlockThreads) st_all |= p.split_status[slot0 + s];
-  st_all = __ballot(st_all != 0) ? 1u : 0u;
-  if (lane == 0) lds.status[wave] = st_all;
+  for (int a = tid; a < n_arr; a += kBlockThreads) st_all |= p.part_status[slot_of(a)];
+  const bool any_bad = __ballot(st_all != 0) != 0;
+  __syncthreads();  // lds.status is rewritten below
+  if (lane == 0) lds.status[wave] = any_bad ? 1u : 0u;
   __syncthreads();
   bool aborted = false;
 #pragma unroll
   for (int w = 0; w < kWavesPerBlock; ++w) aborted |= lds.status[w] != 0;
   if (aborted) {
-    // Recover the exact bits (rare path).
     if (tid == 0) {
       uint32_t bits = 0;
-      for (int s = 0; s < n_splits; ++s) bits |= p.split_status[slot0 + s];
+      for (int a = 0; a < n_arr; ++a) bits |= p.part_status[slot_of(a)];
       p.abort_flags[b] = (uint8_t)bits;
       p.counters[pair] = 0u;
     }
+    __syncthreads();
     return;
   }
   if (tid == 0) {
     p.abort_flags[b] = 0;
     p.counters[pair] = 0u;
   }
-  // weights per (split, head): w = exp2(m_s - M_h)
-  for (int e = tid; e < n_splits * G; e += kBlockThreads) {
-    const int s = e / G, h = e - s * G;
-    lds.w[s][h] = p.split_ml[((slot0 + s) * G + h) * 2];
-  }
-  __syncthreads();
-  if (tid < G) {
+  // per head: M = max over partials, 1/L
+  for (int h = wave; h < G; h += kWavesPerBlock) {
     float M = kNegInf;
-    for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, lds.w[s][tid]);
+    for (int a = lane; a < n_arr; a += 64) M = __builtin_fmaxf(M, p.part_ml[(slot_of(a) * G + h) * 2]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = xor_max(M, off);
     float Ls = 0.f;
-    for (int s = 0; s < n_splits; ++s) Ls += p.split_ml[((slot0 + s) * G + tid) * 2 + 1] * fast_exp2(lds.w[s][tid] - M);
-    lds.head_m[tid] = M;
-    lds.head_inv_l[tid] = v_scale / Ls;
-  }
-  __syncthreads();
-  for (int e = tid; e < n_splits * G; e += kBlockThreads) {
-    const int s = e / G, h = e - s * G;
-    lds.w[s][h] = fast_exp2(lds.w[s][h] - lds.head_m[h]);
-  }
-  __syncthreads();
-  for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
-    const int h = e / D, d = e - h * D;
-    float a0 = 0.f, a1 = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const f32x2_t av = *reinterpret_cast<const f32x2_t*>(p.split_acc + ((slot0 + s) * G + h) * D + d);
-      const float wt = lds.w[s][h];
-      a0 += av[0] * wt;
-      a1 += av[1] * wt;
+    for (int a = lane; a < n_arr; a += 64) {
+      const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (slot_of(a) * G + h) * 2);
+      Ls += ml[1] * fast_exp2(ml[0] - M);
     }
-    const float inv = lds.head_inv_l[h];
-    const uint32_t packed = f32_to_bf16_bits(a0 * inv) | (f32_to_bf16_bits(a1 * inv) << 16);
-    *reinterpret_cast<uint32_t*>(p.out + out_row0 + e) = packed;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) Ls = xor_sum(Ls, off);
+    if (lane == 0) {
+      lds.head_m[h] = M;
+      lds.head_inv_l[h] = v_scale / Ls;
+    }
+  }
+  __syncthreads();
+  float acc0[(kMaxGroup * D) / (2 * kBlockThreads)], acc1[(kMaxGroup * D) / (2 * kBlockThreads)];
+#pragma unroll
+  for (int i = 0; i < (kMaxGroup * D) / (2 * kBlockThreads); ++i) acc0[i] = acc1[i] = 0.f;
+  for (int a0 = 0; a0 < n_arr; a0 += kCombineChunk) {
+    const int na = min(kCombineChunk, n_arr - a0);
+    for (int e = tid; e < na * G; e += kBlockThreads) {
+      const int a = e / G, h = e - a * G;
+      lds.w[a][h] = fast_exp2(p.part_ml[(slot_of(a0 + a) * G + h) * 2] - lds.head_m[h]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (kMaxGroup * D) / (2 * kBlockThreads); ++i) {
+      const int e = 2 * tid + i * 2 * kBlockThreads;
+      if (e < G * D) {
+        const int h = e / D, d = e - h * D;
+        float x0 = acc0[i], x1 = acc1[i];
+        for (int a = 0; a < na; ++a) {
+          const f32x2_t av = *reinterpret_cast<const f32x2_t*>(p.part_acc + (slot_of(a0 + a) * G + h) * D + d);
+          const float wt = lds.w[a][h];
+          x0 += av[0] * wt;
+          x1 += av[1] * wt;
+        }
+        acc0[i] = x0;
+        acc1[i] = x1;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < (kMaxGroup * D) / (2 * kBlockThreads); ++i) {
+    const int e = 2 * tid + i * 2 * kBlockThreads;
+    if (e < G * D) {
+      const int h = e / D;
+      const float inv = lds.head_inv_l[h];
+      store_bf16_pair(p.out + out_row0 + e, acc0[i] * inv, acc1[i] * inv);
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------
+// The kernel: one block per share of the flattened work.
+// ------------------------------------------------------------------------
+template <int KV, int D, int GM, bool MFMA>
+__global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
+  __shared__ MergeLds<D> lds;
+  __shared__ ScanLds sl;
+  const int tid = threadIdx.x;
+  const int k = blockIdx.x;
+  const int max_tokens = p.max_pages << p.log2_page_size;
+  const int64_t hkv = p.num_kv_heads;
+
+  // ---- pass 1: total work; block 0 flags sequences with unusable lengths
+  int64_t mine = 0;
+  for (int b = tid; b < p.batch; b += kBlockThreads) {
+    const int T = seq_tiles(p.seq_lens[b], max_tokens);
+    mine += T;
+    if (T == 0 && k == 0) p.abort_flags[b] = (uint8_t)kAbortMeta;
+  }
+  int64_t seq_total;
+  block_inclusive_scan(mine, sl, tid, seq_total);
+  const int64_t TT = seq_total * hkv;
+  // Never more shares than tiles: every participating block then owns at
+  // least one tile, so every block inside a segment's span arrives.
+  const int64_t nb = min((int64_t)p.num_blocks, TT);
+  if (k >= nb) return;
+  const int64_t r0 = range_start(k, TT, nb), r1 = range_start(k + 1, TT, nb);
+
+  // ---- pass 2: walk the sequences in chunks, process the pieces in [r0, r1)
+  int64_t carry = 0;  // tiles per KV head of all sequences before this chunk
+  for (int c = 0; c < p.batch; c += kBlockThreads) {
+    if (carry * hkv >= r1) break;
+    const int b = c + tid;
+    const int T = b < p.batch ? seq_tiles(p.seq_lens[b], max_tokens) : 0;
+    int64_t chunk_total;
+    const int64_t incl = block_inclusive_scan(T, sl, tid, chunk_total);
+    const int64_t excl = carry + incl - T;
+    sl.tiles[tid] = T;
+    sl.excl[tid] = excl;
+    if (tid == 0) {
+      sl.lo = kBlockThreads;
+      sl.hi = -1;
+    }
+    __syncthreads();
+    const bool hit = T > 0 && excl * hkv < r1 && (excl + T) * hkv > r0;
+    if (hit) {
+      atomicMin(&sl.lo, tid);
+      atomicMax(&sl.hi, tid);
+    }
+    __syncthreads();
+    const int lo = sl.lo, hi = sl.hi;
+    for (int i = lo; i <= hi; ++i) {
+      const int Ti = sl.tiles[i];
+      if (Ti == 0) continue;
+      const int bi = c + i;
+      const int64_t seq_lo = sl.excl[i] * hkv;
+      const int L = p.seq_lens[bi];
+      const int64_t g_first = r0 > seq_lo ? (r0 - seq_lo) / Ti : 0;
+      const int64_t g_last = min((int64_t)(hkv - 1), (r1 - 1 - seq_lo) / Ti);
+      for (int64_t g = g_first; g <= g_last; ++g) {
+        const int64_t seg_lo = seq_lo + g * Ti;
+        const int t_lo = (int)(max(seg_lo, r0) - seg_lo);
+        const int t_hi = (int)(min(seg_lo + Ti, r1) - seg_lo);
+        process_piece<KV, D, GM, MFMA>(p, lds, bi, (int)g, L, Ti, t_lo, t_hi, seg_lo, r0, TT, nb, k, tid);
+      }
+    }
+    carry += chunk_total;
+    __syncthreads();  // sl is rewritten by the next chunk
   }
 }
 
 template <int KV, int D, int GM, bool MFMA>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  dim3 grid(p.splits, p.num_kv_heads, p.batch);
-  hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), grid, dim3(kBlockThreads), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), dim3(p.num_blocks), dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
 }
 

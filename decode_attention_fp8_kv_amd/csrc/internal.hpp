@@ -35,30 +35,26 @@ struct DecodeParams {
   const uint32_t* expected_tags;    // [B][max_pages] or null
   uint16_t* out;                    // bf16 [B][Hq][D]
   uint8_t* abort_flags;             // [B]
-  uint32_t* counters;               // [B*Hkv]   arrivals per (sequence, KV head)
-  uint32_t* split_status;           // [B*Hkv*S] abort bits seen by each split
-  float* split_ml;                  // [B*Hkv*S][G][2]  running max (log2 domain), sum
-  float* split_acc;                 // [B*Hkv*S][G][D]  unnormalized output
+  uint32_t* counters;               // [B*Hkv] arrivals per (sequence, KV head); zero between calls
+  uint32_t* part_status;            // [2*num_blocks]        abort bits of each partial piece
+  float* part_ml;                   // [2*num_blocks][G][2]  running max (log2 domain), sum
+  float* part_acc;                  // [2*num_blocks][G][D]  unnormalized output
   int32_t batch, num_q_heads, num_kv_heads, group, max_pages, num_pages;
   int32_t log2_page_size;
-  int32_t tiles_per_split, splits;  // S = splits (per sequence, maximum)
+  int32_t num_blocks;               // grid size; block k owns an equal share of all tiles
   float qk_scale_log2;              // softmax_scale * k_scale * log2(e)
   float v_scale;                    // folded into the final normalization
 };
 
-// Work decomposition chosen on the host from sizes only (no device reads).
-struct SplitPlan {
-  int32_t tiles_per_split;
-  int32_t splits;
-};
-SplitPlan plan_splits(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages,
-                      int32_t num_splits);
+// Grid size chosen on the host from sizes only (no device reads).
+int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages,
+                    int32_t num_blocks);
 
 struct WorkspaceLayout {
-  size_t counters, split_status, split_ml, split_acc, total;
+  size_t counters, part_status, part_ml, part_acc, total;
 };
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t splits);
+                                 int32_t head_dim, int32_t num_blocks);
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,

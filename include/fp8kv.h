@@ -120,14 +120,14 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new,
 
 /*
  * paged_decode_attn_workspace_size -- bytes of device workspace that
- * paged_decode_attn needs for these sizes (0 never; always a multiple of 256).
- * num_splits has the meaning it has in paged_decode_attn.  Returns 0 if the
- * sizes are invalid.
+ * paged_decode_attn needs for these sizes (a multiple of 256; at most a few
+ * MiB).  num_blocks has the meaning it has in paged_decode_attn.  Returns 0
+ * if the sizes are invalid.
  */
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t page_size, int32_t max_pages,
-                                        int32_t num_splits);
+                                        int32_t num_blocks);
 
 /*
  * paged_decode_attn -- one decode step of attention for a batch of
@@ -161,9 +161,12 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *                  leaves its counters at zero again, so it can be reused
  *                  without clearing.  Calls sharing a workspace must be
  *                  ordered (same stream).
- *   num_splits     0 = choose automatically; n > 0 = split each sequence's
- *                  tokens into about n contiguous ranges (flash-decoding),
- *                  clamped to what the length allows.
+ *   num_blocks     0 = choose automatically; n > 0 = use n workgroups
+ *                  (at most 65535).  The batch's work -- every (sequence,
+ *                  KV head, 64-token tile) -- is cut into n equal contiguous
+ *                  shares, so long sequences are split across workgroups
+ *                  (flash-decoding) and merged exactly; the result does not
+ *                  depend on n beyond floating-point rounding.
  *
  * Tag rule: for every page slot j < ceil(L / page_size) (the partial last
  * page included), the page id p = page_table[b*max_pages + j] must lie in
@@ -182,7 +185,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       void* workspace, size_t workspace_bytes,
                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t page_size, int32_t num_pages,
-                      float softmax_scale, int32_t num_splits, void* stream);
+                      float softmax_scale, int32_t num_blocks, void* stream);
 
 /*
  * paged_decode_attn_path -- which kernel family paged_decode_attn uses for a

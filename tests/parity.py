@@ -82,7 +82,7 @@ def oracle_fill(w, kv_dtype, include_new=True):
     return kc, vc
 
 
-def gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=True, num_splits=0, seq_lens=None, page_table=None,
+def gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=True, num_blocks=0, seq_lens=None, page_table=None,
                page_tags=None, expected_tags=None):
     seq_lens = w.seq_lens if seq_lens is None else seq_lens
     page_table = w.page_table if page_table is None else page_table
@@ -93,13 +93,13 @@ def gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=True, num_splits=0, seq_lens=No
     out = out.view(torch.bfloat16)
     flags = torch.full((w.batch,), 0xEE, dtype=torch.uint8, device=dev)
     ws = fk.alloc_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
-                            page_table.shape[1], num_splits, device=dev)
+                            page_table.shape[1], num_blocks, device=dev)
     tags = torch.from_numpy(page_tags.view(np.int32)).to(dev) if tags_on else None
     exp = torch.from_numpy(np.ascontiguousarray(expected_tags).view(np.int32)).to(dev) if tags_on else None
     fk.paged_decode_attn(w.q.to(dev).contiguous(), kc, vc, torch.from_numpy(page_table).to(dev),
                          torch.from_numpy(np.asarray(seq_lens, np.int32)).to(dev), out, flags, ws,
                          kv_dtype=kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale, page_tags=tags,
-                         expected_tags=exp, softmax_scale=w.softmax_scale, num_splits=num_splits)
+                         expected_tags=exp, softmax_scale=w.softmax_scale, num_blocks=num_blocks)
     torch.cuda.synchronize(dev)
     return W.bits_u16(out), flags.cpu().numpy(), ws
 

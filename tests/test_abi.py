@@ -70,12 +70,12 @@ FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
 def _decode(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, kv_dtype=0, ks=1.0, vs=1.0, pt=FAKE, max_pages=8, lens=FAKE,
              tags=None, exp=None, out=FAKE, abort=FAKE, ws=FAKE, ws_bytes=1 << 30, batch=2, hq=8, hkv=2,
-             d=64, ps=16, num_pages=64, sm=0.125, splits=0)
+             d=64, ps=16, num_pages=64, sm=0.125, blocks=0)
     a.update(kw)
     return lib.paged_decode_attn(a["q"], a["k"], a["v"], a["kv_dtype"], a["ks"], a["vs"], a["pt"],
                                  a["max_pages"], a["lens"], a["tags"], a["exp"], a["out"], a["abort"],
                                  a["ws"], a["ws_bytes"], a["batch"], a["hq"], a["hkv"], a["d"], a["ps"],
-                                 a["num_pages"], a["sm"], a["splits"], None)
+                                 a["num_pages"], a["sm"], a["blocks"], None)
 
 
 def test_decode_validation_codes(lib):
@@ -88,7 +88,8 @@ def test_decode_validation_codes(lib):
     assert _decode(lib, hq=7, hkv=2) == E["SHAPE"]
     assert _decode(lib, num_pages=0) == E["SHAPE"]
     assert _decode(lib, max_pages=-1) == E["SHAPE"]
-    assert _decode(lib, splits=-1) == E["SHAPE"]
+    assert _decode(lib, blocks=-1) == E["SHAPE"]
+    assert _decode(lib, batch=65535, hkv=65535, hq=65535, max_pages=1 << 20, ps=16) == E["SHAPE"]
     assert _decode(lib, batch=70000) == E["SHAPE"]
     assert _decode(lib, d=96) == E["UNSUPPORTED"]
     assert _decode(lib, ps=24) == E["UNSUPPORTED"]

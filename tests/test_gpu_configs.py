@@ -6,7 +6,7 @@ At these sizes the oracle cannot redo a whole batch quickly, so:
   with the oracle's own quantization of that sequence's rows, and every
   query head's output with the oracle's fp64 attention over those bytes;
 * aborted sequences' outputs must be untouched.
-The decode runs with the automatic split plan (num_splits = 0), the launch
+The decode runs with the automatic work plan (num_blocks = 0), the launch
 configuration the benchmark times.
 """
 

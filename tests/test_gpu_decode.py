@@ -23,12 +23,12 @@ pytestmark = pytest.mark.gpu
 FP8, BF16 = fk.KV_FP8_E4M3, fk.KV_BF16
 
 
-def _run_case(w, kv_dtype, dev, tags_on=True, num_splits=0, **over):
+def _run_case(w, kv_dtype, dev, tags_on=True, num_blocks=0, **over):
     kc, vc = gpu_fill(w, kv_dtype, dev)
     okc, ovc = oracle_fill(w, kv_dtype)
     assert np.array_equal(pool_bits(kc), okc), "K cache bytes differ from the oracle"
     assert np.array_equal(pool_bits(vc), ovc), "V cache bytes differ from the oracle"
-    out, flags, ws = gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=tags_on, num_splits=num_splits, **over)
+    out, flags, ws = gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=tags_on, num_blocks=num_blocks, **over)
     ref, rflags = oracle_decode(w, kv_dtype, okc, ovc, tags_on=tags_on, **over)
     assert np.array_equal(flags, rflags), f"abort flags {flags} != oracle {rflags}"
     compare_outputs(out, ref, flags)
@@ -72,12 +72,14 @@ def test_shapes(gpu_device, shape, kv_dtype):
     _run_case(w, kv_dtype, gpu_device)
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 32, 300])
+@pytest.mark.parametrize("num_blocks", [1, 2, 3, 7, 32, 300, 911, 912, 913, 1000, 5000])
 @pytest.mark.parametrize("hq,hkv", [(64, 8), (8, 2)])
-def test_split_counts(gpu_device, num_splits, hq, hkv):
-    say(f"splits={num_splits} hq={hq} hkv={hkv}")
-    w = W.make_custom([5000, 2100, 64, 1], hq, hkv, 128, 64, seed=num_splits)
-    _run_case(w, FP8, gpu_device, num_splits=num_splits)
+def test_block_counts(gpu_device, num_blocks, hq, hkv):
+    # lengths [5000, 2100, 64, 1] make 79 + 33 + 1 + 1 = 114 tiles per KV head:
+    # 912 tiles at 8 KV heads; the grid may have fewer, as many or more blocks
+    say(f"blocks={num_blocks} hq={hq} hkv={hkv}")
+    w = W.make_custom([5000, 2100, 64, 1], hq, hkv, 128, 64, seed=num_blocks)
+    _run_case(w, FP8, gpu_device, num_blocks=num_blocks)
 
 
 def test_deterministic_and_layout_invariant(gpu_device):
@@ -123,17 +125,17 @@ def test_tag_and_metadata_cases(gpu_device):
         compare_outputs(out, ref, flags)
 
 
-@pytest.mark.parametrize("num_splits", [1, 5])
-def test_mismatch_in_every_split_position(gpu_device, num_splits):
+@pytest.mark.parametrize("num_blocks", [1, 5])
+def test_mismatch_in_every_page_position(gpu_device, num_blocks):
     # one stale page at a time, in each page slot of a long sequence
     w = W.make_custom([1100, 90], 8, 1, 128, 64, seed=21)
     kc, vc = gpu_fill(w, FP8, gpu_device)
     okc, ovc = oracle_fill(w, FP8)
     for j in range(0, 18):
-        say(f"stale page slot {j} splits={num_splits}")
+        say(f"stale page slot {j} blocks={num_blocks}")
         exp = w.expected_tags.copy()
         exp[0, j] ^= np.uint32(0x80000000)
-        out, flags, _ = gpu_decode(w, FP8, kc, vc, gpu_device, expected_tags=exp, num_splits=num_splits)
+        out, flags, _ = gpu_decode(w, FP8, kc, vc, gpu_device, expected_tags=exp, num_blocks=num_blocks)
         assert flags.tolist() == [1, 0]
         assert np.all(out[0] == OUT_SENTINEL)
         ref, rflags = oracle_decode(w, FP8, okc, ovc, expected_tags=exp)
