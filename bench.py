@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
 WORKLOAD = "conc32"
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_counters.txt")
 KERNEL_SOURCES = ["decode_attention_fp8_kv_amd/csrc/decode_attn.hip", "decode_attention_fp8_kv_amd/csrc/common.hpp",
                   "decode_attention_fp8_kv_amd/csrc/internal.hpp", "decode_attention_fp8_kv_amd/csrc/api.cpp"]
 
@@ -152,6 +152,29 @@ def tag_overhead(case, iters=100):
     }
 
 
+def copy_bandwidth(dev, nbytes=2 << 30, reps=10):
+    """Device-to-device copy of `nbytes` (read + write counted): the box's
+    practical streaming rate, reported beside the roofline, never in its place.
+    Its kernel is also the plain copy of known size used to scale the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize(dev)
+    gbps = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbps
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     for whole sequences taken in order, time one decode step (append of the new
@@ -204,6 +227,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device-copy bandwidth measurement")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: decode sequences shard across GPUs with no exchange "
@@ -217,6 +241,7 @@ def main():
 
     dev = torch.device("cuda:0")
     fk.load_library()
+    copy_gbps = None if args.no_copy else copy_bandwidth(dev)
     w = W.make(WORKLOAD, device=dev)
     res = {}
     for kv, name in ((fk.KV_FP8_E4M3, "fp8"), (fk.KV_BF16, "bf16")):
@@ -247,10 +272,14 @@ def main():
     f = res["fp8"]
     traffic = None
     if os.path.exists(PROFILE_COUNTERS):
+        prof = {}
         with open(PROFILE_COUNTERS) as fh:
-            prof = json.load(fh)
-        if prof.get("kernel_source_hash") == kernel_source_hash():
-            traffic = prof.get("traffic_bytes_per_launch")
+            for ln in fh:
+                if ":" in ln and not ln.startswith("#"):
+                    key, val = ln.split(":", 1)
+                    prof[key.strip()] = val.strip()
+        if prof.get("kernel_source_hash") == kernel_source_hash() and "traffic_bytes_per_launch" in prof:
+            traffic = int(float(prof["traffic_bytes_per_launch"]))
     line = {
         "metric": "decode-attn tokens/s + effective KV GB/s (% HBM peak), FP8 vs BF16 KV, 1 GPU",
         "value": round(f["value"], 1),
@@ -285,6 +314,7 @@ def main():
             "traffic": traffic,
         },
         "tag_check": res.get("tags"),
+        "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }
     if "bf16" in res:
         b = res["bf16"]

@@ -144,6 +144,11 @@ struct MfmaTile {
   uint32_t k[4][G_::KQ / 4];   // token block bb: this lane's quarter row
   uint32_t v[16][G_::VW];      // 16 tokens: this lane's D/16 dims
 };
+// FP8 cache: only K is held in registers; V streams through LDS (see below).
+template <int D>
+struct MfmaTile<0, D> {
+  uint32_t k[4][Geo<0, D>::KQ / 4];
+};
 
 template <int KV, int D>
 struct MfmaState {
@@ -161,8 +166,10 @@ __device__ __forceinline__ void mfma_load_k(MfmaTile<KV, D>& t, const uint8_t* k
 template <int KV, int D>
 __device__ __forceinline__ void mfma_load_v(MfmaTile<KV, D>& t, const uint8_t* vp) {
   using G_ = Geo<KV, D>;
+  if constexpr (KV != 0) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) load_words<G_::VW>(vp + i * G_::ROW, t.v[i]);
+    for (int i = 0; i < 16; ++i) load_words<G_::VW>(vp + i * G_::ROW, t.v[i]);
+  }
 }
 
 // S^T for the tile's 64 tokens: s[bb][r] = score of token 16*(lane/16) + 4*bb + r
@@ -278,6 +285,126 @@ __device__ __forceinline__ void mfma_softmax_pv(MfmaTile<KV, D>& t, MfmaState<KV
       }
     }
   }
+}
+
+// ------------------------------------------------------------------------
+// FP8 V through LDS.
+//
+// A 64-token V tile of one (page, KV head) is 64 rows of D bytes.  Each wave
+// copies its next tile global -> LDS with global_load_lds_dwordx4 (lane j of
+// an instruction lands at LDS base + 16 j, so 1 KiB per instruction and no
+// VGPRs in flight), then reads it back with ds_read_b64_tr_b8, which
+// transposes 8x16-byte blocks across each 16-lane group: lane j receives byte
+// j of 8 consecutive 16-byte rows -- exactly the V^T operand of the PV MFMA
+// (one dim, 8 tokens).  16-byte chunks are XOR-swizzled with the row index
+// so that the 8 rows of a read fall in different LDS banks.
+//
+// The compiler waits for every outstanding LDS DMA before any LDS read, so
+// the order per tile is: read tile i out of LDS, then start the copy of tile
+// i+1 into the same buffer, then compute tile i.
+// ------------------------------------------------------------------------
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+#define FP8KV_LDS(ptr) ((__attribute__((address_space(3))) void*)(ptr))
+
+// Physical page of 16-token group `grp16` of the round's tile `i`, for a
+// wave-uniform group (scalar read of the page list).
+__device__ __forceinline__ int page_of_uniform(const PageRound& pr, int i, int grp16) {
+  if (pr.log2ps >= 6) return __builtin_amdgcn_readlane(pr.pid, i);
+  return __builtin_amdgcn_readlane(pr.pid, (i << pr.ppt_log2) + (grp16 >> (pr.log2ps - 4)));
+}
+
+template <int D>
+__device__ __forceinline__ void v_tile_to_lds(const DecodeParams& p, const PageRound& pr, int i, int tile_abs, int g,
+                                              int lane, uint8_t* stage) {
+  constexpr int ROW = Geo<0, D>::ROW;       // bytes per token row
+  constexpr int CH = ROW / 16;              // 16-byte chunks per row
+  constexpr int RPI = 64 / CH;              // rows per DMA instruction (1 KiB)
+  const int ps_mask = (1 << pr.log2ps) - 1;
+  const int base_tok = tile_abs << 6;
+  const int row_in = lane / CH, c = lane % CH;
+#pragma unroll
+  for (int m = 0; m < kTileTokens / RPI; ++m) {
+    const int t = m * RPI + row_in;                       // token within the tile
+    const int pid = page_of_uniform(pr, i, (m * RPI) >> 4);
+    const uint8_t* src = row_ptr(p.v_cache, pid, g, p.num_kv_heads, pr.log2ps, (base_tok + t) & ps_mask, ROW) +
+                         16 * (c ^ (t & (CH - 1)));
+    __builtin_amdgcn_global_load_lds(src, FP8KV_LDS(stage + m * 1024), 16, 0, 0);
+  }
+}
+
+// vt[ks][nb]: 8 e4m3 codes of dim 16*nb + lane%16 for tokens 16*(lane/16) + 8*ks + 0..7.
+template <int D>
+__device__ __forceinline__ void v_tile_from_lds(const uint8_t* stage, int lane, v2i_t (&vt)[2][Geo<0, D>::NB]) {
+  constexpr int ROW = Geo<0, D>::ROW;
+  constexpr int CH = ROW / 16;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int t = 16 * (lane >> 4) + 8 * ks + ((lane & 15) >> 1);
+#pragma unroll
+    for (int nb = 0; nb < Geo<0, D>::NB; ++nb) {
+      const uint8_t* a = stage + t * ROW + 16 * (nb ^ (t & (CH - 1))) + 8 * (lane & 1);
+      vt[ks][nb] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i_t*)(a));
+    }
+  }
+}
+
+// Online softmax update and O^T += V^T P^T for an FP8 tile whose V operands
+// came from LDS (vt); same score layout as mfma_softmax_pv.
+template <int D>
+__device__ __forceinline__ void mfma_softmax_pv_lds(MfmaState<0, D>& st, f32x4_t s[4], v2i_t (&vt)[2][Geo<0, D>::NB],
+                                                    int valid, float scale_log2, int lane) {
+  using G_ = Geo<0, D>;
+  const int vg = lane >> 4;
+  float mt = kNegInf;
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = s[bb][r] * scale_log2;
+      if (valid < kTileTokens && 16 * vg + 4 * bb + r >= valid) x = kNegInf;
+      s[bb][r] = x;
+      mt = __builtin_fmaxf(mt, x);
+    }
+  mt = xor_max(mt, 16);
+  mt = xor_max(mt, 32);
+  const float m_new = __builtin_fmaxf(st.m, mt);
+  const float m_use = m_new == kNegInf ? 0.f : m_new;
+  const float alpha = fast_exp2(st.m - m_use);
+  st.m = m_new;
+  st.l *= alpha;
+#pragma unroll
+  for (int nb = 0; nb < G_::NB; ++nb) st.acc[nb] *= alpha;
+  f16x8_t bop[2];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = fast_exp2(s[bb][r] - m_use);
+      st.l += e;
+      bop[bb >> 1][4 * (bb & 1) + r] = (_Float16)e;
+    }
+  // Rows past the sequence end may hold anything (even NaN codes): zero them.
+  if (valid < kTileTokens) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int t0 = 16 * vg + 8 * ks;  // token of byte 0
+      const int n_ok = min(max(valid - t0, 0), 8);
+      const uint64_t keep = n_ok >= 8 ? ~0ull : ((1ull << (8 * n_ok)) - 1ull);
+#pragma unroll
+      for (int nb = 0; nb < G_::NB; ++nb) {
+        vt[ks][nb].x &= (int)(uint32_t)keep;
+        vt[ks][nb].y &= (int)(uint32_t)(keep >> 32);
+      }
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int nb = 0; nb < G_::NB; ++nb) {
+      const f16x8_t aop = e4m3x8_to_f16x8((uint32_t)vt[ks][nb].x, (uint32_t)vt[ks][nb].y);
+      st.acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[ks], st.acc[nb], 0, 0, 0);
+    }
 }
 
 // ------------------------------------------------------------------------
@@ -456,7 +583,8 @@ __device__ __forceinline__ void compute_tile(typename WaveState<KV, D, GM, MFMA>
 template <int KV, int D, int GM, bool MFMA>
 __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g, int L, int first_tile,
                                              int n_wave_tiles, typename WaveState<KV, D, GM, MFMA>::T& st,
-                                             int lane) {
+                                             int lane, uint8_t* vstage) {
+  constexpr bool kVlds = MFMA && KV == 0;  // FP8 V streams through LDS
   using Tile = typename WaveState<KV, D, GM, MFMA>::Tile;
   const int log2ps = p.log2_page_size;
   const int ppt_log2 = log2ps < 6 ? 6 - log2ps : 0;
@@ -496,27 +624,57 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
       // Speculative: page ids are range-checked; data is not used before the tag ballot.
       tile_pointers<KV, D, GM, MFMA>(p, pr, 0, first_tile + 4 * r0, g, lane, kp, vp);
       load_tile<KV, D, GM, MFMA>(ta, kp, vp);
+      if constexpr (kVlds) v_tile_to_lds<D>(p, pr, 0, first_tile + 4 * r0, g, lane, vstage);
     }
     const bool any_mismatch = __any(actual != expected);
     status |= (any_bad ? kAbortMeta : 0u) | (any_mismatch ? kAbortTag : 0u);
-    if (status != 0) continue;  // keep checking later rounds; compute nothing
+    if (status != 0) {
+      if constexpr (kVlds) __builtin_amdgcn_s_waitcnt(0);  // no copy may still be landing in LDS
+      continue;  // keep checking later rounds; compute nothing
+    }
 
+    if constexpr (kVlds) {
+      // Per tile i: V(i) out of LDS; start V(i+1) into LDS; QK(i) from the K
+      // registers; then start K(i+1) into those registers; softmax + PV(i).
+      // Both next-tile streams are in flight while tile i is computed, and the
+      // next iteration's LDS read waits for them (the compiler waits for all
+      // LDS copies before an LDS read).  The last iteration re-reads the
+      // round's last tile so that no load sits under a condition.
+      const float sl = p.qk_scale_log2;
+      v2i_t vt[2][Geo<0, D>::NB];
+      for (int i = 0; i < rt; ++i) {
+        const int t0 = first_tile + 4 * (r0 + i);
+        const int n1 = min(i + 1, rt - 1);
+        v_tile_from_lds<D>(vstage, lane, vt);
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): tile i is out of LDS before it is overwritten
+        __builtin_amdgcn_sched_barrier(0);
+        v_tile_to_lds<D>(p, pr, n1, first_tile + 4 * (r0 + n1), g, lane, vstage);
+        f32x4_t sc[4];
+        mfma_qk<KV, D>(ta, st, sc);
+        __builtin_amdgcn_sched_barrier(0);
+        tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + 4 * (r0 + n1), g, lane, kp, vp);
+        mfma_load_k<KV, D>(ta, kp);
+        mfma_softmax_pv_lds<D>(st, sc, vt, min(L - (t0 << 6), kTileTokens), sl, lane);
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // the last (redundant) copy has landed before LDS is reused
+    } else {
+    // Tile i is computed while tile i+1 loads.  The prefetch is issued on
+    // every iteration (the last one re-reads the round's last tile, which is
+    // still in cache): a prefetch under a condition would make the compiler
+    // wait for it inside the current tile's math, serializing the pipeline.
     const float sl = p.qk_scale_log2;
-    for (int i = 0; i < rt;) {
+    for (int i = 0; i < rt; i += 2) {
+      const int n1 = min(i + 1, rt - 1);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + 4 * (r0 + n1), g, lane, kp, vp);
+      load_tile<KV, D, GM, MFMA>(tb, kp, vp);
       const int t0 = first_tile + 4 * (r0 + i);
-      if (i + 1 < rt) {
-        tile_pointers<KV, D, GM, MFMA>(p, pr, i + 1, t0 + 4, g, lane, kp, vp);
-        load_tile<KV, D, GM, MFMA>(tb, kp, vp);
-      }
       compute_tile<KV, D, GM, MFMA>(ta, st, min(L - (t0 << 6), kTileTokens), sl, lane);
-      if (++i >= rt) break;
-      const int t1 = t0 + 4;
-      if (i + 1 < rt) {
-        tile_pointers<KV, D, GM, MFMA>(p, pr, i + 1, t1 + 4, g, lane, kp, vp);
-        load_tile<KV, D, GM, MFMA>(ta, kp, vp);
-      }
-      compute_tile<KV, D, GM, MFMA>(tb, st, min(L - (t1 << 6), kTileTokens), sl, lane);
-      ++i;
+      if (i + 1 >= rt) break;
+      const int n2 = min(i + 2, rt - 1);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, n2, first_tile + 4 * (r0 + n2), g, lane, kp, vp);
+      load_tile<KV, D, GM, MFMA>(ta, kp, vp);
+      compute_tile<KV, D, GM, MFMA>(tb, st, min(L - ((t0 + 4) << 6), kTileTokens), sl, lane);
+    }
     }
   }
   return status;
@@ -535,7 +693,12 @@ __device__ __forceinline__ void export_state(MfmaState<KV, D>& st, MergeLds<D>& 
 #pragma unroll
     for (int nb = 0; nb < G_::NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lds.acc[wave][h][G_::NB * (4 * (lane >> 4) + r) + nb] = st.acc[nb][r];
+      for (int r = 0; r < 4; ++r) {
+        // FP8 (V^T read from LDS): row = dim 16*nb + 4*(lane/16) + r;
+        // BF16 (V^T built in registers): row = dim NB*(4*(lane/16) + r) + nb
+        const int d = KV == 0 ? 16 * nb + 4 * (lane >> 4) + r : G_::NB * (4 * (lane >> 4) + r) + nb;
+        lds.acc[wave][h][d] = st.acc[nb][r];
+      }
     if (lane < 16) {
       lds.m[wave][h] = st.m;
       lds.l[wave][h] = l;
@@ -649,9 +812,9 @@ __device__ __forceinline__ void store_bf16_pair(uint16_t* dst, float a0, float a
 // One piece: tiles [t_lo, t_hi) of segment (b, g), whose flattened range is
 // [seg_lo, seg_lo + T).  Ends with a block barrier (LDS is reused next).
 template <int KV, int D, int GM, bool MFMA>
-__device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>& lds, int b, int g, int L, int T,
-                                              int t_lo, int t_hi, int64_t seg_lo, int64_t r0, int64_t TT,
-                                              int64_t nb, int k, int tid) {
+__device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>& lds, uint8_t* vstage, int b, int g,
+                                              int L, int T, int t_lo, int t_hi, int64_t seg_lo, int64_t r0,
+                                              int64_t TT, int64_t nb, int k, int tid) {
   const int lane = tid & 63, wave = tid >> 6;
   const int G = p.group;
   const int count = t_hi - t_lo;
@@ -695,7 +858,7 @@ __device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>
     }
   }
 
-  const uint32_t wave_status = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo + wave, n_wave_tiles, st, lane);
+  const uint32_t wave_status = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo + wave, n_wave_tiles, st, lane, vstage);
   export_state(st, lds, wave, lane, G);
   if (lane == 0) lds.status[wave] = wave_status;
   __syncthreads();
@@ -838,9 +1001,12 @@ __device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>
 // The kernel: one block per share of the flattened work.
 // ------------------------------------------------------------------------
 template <int KV, int D, int GM, bool MFMA>
-__global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kBlockThreads, (MFMA && KV == 0) ? 2 : 1) void decode_kernel(DecodeParams p) {
   __shared__ MergeLds<D> lds;
   __shared__ ScanLds sl;
+  // FP8 MFMA family: one 64-token V tile per wave staged in LDS
+  constexpr int kStage = (MFMA && KV == 0) ? kTileTokens * D : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t vstage_all[kWavesPerBlock][kStage];
   const int tid = threadIdx.x;
   const int k = blockIdx.x;
   const int max_tokens = p.max_pages << p.log2_page_size;
@@ -897,7 +1063,8 @@ __global__ __launch_bounds__(kBlockThreads) void decode_kernel(DecodeParams p) {
         const int64_t seg_lo = seq_lo + g * Ti;
         const int t_lo = (int)(max(seg_lo, r0) - seg_lo);
         const int t_hi = (int)(min(seg_lo + Ti, r1) - seg_lo);
-        process_piece<KV, D, GM, MFMA>(p, lds, bi, (int)g, L, Ti, t_lo, t_hi, seg_lo, r0, TT, nb, k, tid);
+        process_piece<KV, D, GM, MFMA>(p, lds, vstage_all[tid >> 6], bi, (int)g, L, Ti, t_lo, t_hi, seg_lo, r0, TT,
+                                       nb, k, tid);
       }
     }
     carry += chunk_total;
