@@ -148,12 +148,12 @@ def paged_decode_attn_path(num_q_heads, num_kv_heads) -> int:
 
 def alloc_workspace(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages, num_blocks=0,
                     device="cuda"):
-    """A zero-filled workspace of the size the library asks for (allocated by torch)."""
+    """A workspace of the size the library asks for (allocated by torch; needs no initialization)."""
     n = paged_decode_attn_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages,
                                          num_blocks)
     if n == 0:
         raise ValueError("invalid sizes for a workspace")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flags, workspace, *,

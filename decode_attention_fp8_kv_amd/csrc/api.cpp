@@ -36,8 +36,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
-constexpr int64_t kResidentBlocks = 512;  // 2 blocks of 4 waves on each of MI355X's 256 CUs
-constexpr int64_t kMinTilesPerBlock = 16; // below this, fewer blocks: merge cost beats parallelism
+constexpr int64_t kComputeUnits = 256;    // MI355X; the default grid keeps every block resident
+constexpr int32_t kMaxBlocksPerCu = 2;
+constexpr int64_t kMinTilesPerWave = 8;   // below this, fewer waves: merge cost beats parallelism
 constexpr int64_t kMaxBlocks = 65535;
 constexpr int64_t kMaxTotalTiles = int64_t(1) << 40;
 
@@ -50,23 +51,25 @@ int64_t max_total_tiles(int32_t batch, int32_t num_kv_heads, int32_t page_size, 
 
 }  // namespace
 
-int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages, int32_t num_blocks) {
+int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages, int32_t num_blocks,
+                    int32_t blocks_per_cu) {
   int64_t nb = num_blocks;
   if (nb <= 0) {
     const int64_t bound = max_total_tiles(batch, num_kv_heads, page_size, max_pages);
-    nb = std::min(kResidentBlocks, (bound + kMinTilesPerBlock - 1) / kMinTilesPerBlock);
+    const int64_t per_block = kMinTilesPerWave * kWavesPerBlock;
+    nb = std::min(kComputeUnits * blocks_per_cu, (bound + per_block - 1) / per_block);
   }
   return (int32_t)std::max<int64_t>(1, std::min(nb, kMaxBlocks));
 }
 
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t num_blocks) {
-  const size_t pairs = (size_t)batch * num_kv_heads;
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
-  const size_t slots = 2 * (size_t)num_blocks;
+  const size_t segs = (size_t)batch * num_kv_heads;
+  const size_t slots = 2 * (size_t)num_blocks * kWavesPerBlock;  // two partial slots per wave
   WorkspaceLayout w;
-  w.counters = 0;
-  w.part_status = round_up(pairs * sizeof(uint32_t), 256);
+  w.seg_desc = 0;
+  w.part_status = round_up(segs * sizeof(uint64_t), 256);
   w.part_ml = w.part_status + round_up(slots * sizeof(uint32_t), 256);
   w.part_acc = w.part_ml + round_up(slots * group * 2 * sizeof(float), 256);
   w.total = w.part_acc + round_up(slots * group * head_dim * sizeof(float), 256);
@@ -139,7 +142,7 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int3
                                         int32_t page_size, int32_t max_pages, int32_t num_blocks) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_blocks < 0) return 0;
   if (num_q_heads % num_kv_heads != 0 || !supported_head_dim(head_dim) || log2_page_size(page_size) < 0) return 0;
-  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks);
+  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kMaxBlocksPerCu);
   return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb).total;
 }
 
@@ -161,7 +164,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_pages <= 0 || num_blocks < 0)
     return FP8KV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return FP8KV_ERR_SHAPE;
-  if (batch > 65535 || num_kv_heads > 65535) return FP8KV_ERR_SHAPE;
+  if (batch > 65535 || num_kv_heads > 65535 || (int64_t)batch * num_kv_heads > INT32_MAX) return FP8KV_ERR_SHAPE;
   const int32_t group = num_q_heads / num_kv_heads;
   if (group > kMaxGroup || !supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
   const int l2ps = log2_page_size(page_size);
@@ -177,7 +180,10 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   if (!aligned(q, 16) || !aligned(out, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(workspace, 256))
     return FP8KV_ERR_ALIGN;
-  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks);
+  const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
+  // resident blocks per CU: the FP8 MFMA kernel runs 2 waves per SIMD, the others 1
+  const int32_t per_cu = (mfma && kv_dtype == FP8KV_KV_FP8_E4M3) ? 2 : 1;
+  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, per_cu);
   const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb);
   if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;
 
@@ -193,7 +199,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   p.out = out;
   p.abort_flags = abort_flags;
   uint8_t* base = static_cast<uint8_t*>(workspace);
-  p.counters = reinterpret_cast<uint32_t*>(base + ws.counters);
+  p.seg_desc = reinterpret_cast<uint64_t*>(base + ws.seg_desc);
   p.part_status = reinterpret_cast<uint32_t*>(base + ws.part_status);
   p.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
   p.part_acc = reinterpret_cast<float*>(base + ws.part_acc);
@@ -212,7 +218,6 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
     p.qk_scale_log2 = (float)((double)softmax_scale * log2e);
     p.v_scale = 1.0f;
   }
-  const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
   return record_hip(launch_decode(p, kv_dtype, head_dim, mfma, static_cast<hipStream_t>(stream)));
 }
 

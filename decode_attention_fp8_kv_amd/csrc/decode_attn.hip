@@ -18,17 +18,16 @@
 // Work decomposition
 // ------------------
 // The batch's work is the flattened list of (sequence, KV head, 64-token
-// tile) triples; a 1-D grid of num_blocks blocks of 256 threads (4 waves)
-// cuts it into equal contiguous shares (see "The balanced schedule" below),
-// so every block streams the same number of bytes whatever the length mix
-// and long sequences are split across blocks (flash-decoding).  Within a
-// piece of one (sequence, KV head), the 4 waves take every 4th tile and each
-// keeps its own online-softmax state (running max m, sum l, unnormalized
-// acc); the waves merge through LDS.  A piece that is a whole segment is
-// finished in place; a partial piece is stored in the workspace and the
-// block that arrives last for its (sequence, KV head) merges all partials
-// (log-sum-exp), writes the output and the abort flag, and resets the
-// arrival counter to zero.
+// tile) triples.  A 1-D grid of blocks of 4 independent waves cuts it into
+// equal contiguous shares, one per wave (see "The balanced schedule"), so
+// every wave streams the same number of bytes whatever the length mix and
+// long sequences are split across waves (flash-decoding).  A wave keeps an
+// online-softmax state (running max m, sum l, unnormalized acc) per piece
+// of one (sequence, KV head); a piece that is a whole segment is finished in
+// registers, a partial piece is published to the workspace and the merge
+// kernel (one block per (sequence, KV head)) combines its partials
+// (log-sum-exp) in a second kernel and writes the output and the abort
+// flag.  No wave ever waits for another.
 
 // Per wave and tile (MFMA family, group of 5..16 query heads per KV head):
 //   * K rows: lane l loads a quarter of one token's row (bytes of dims
@@ -61,23 +60,6 @@ namespace {
 constexpr uint32_t kAbortTag = 1u;
 constexpr uint32_t kAbortMeta = 2u;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kCombineChunk = 256;
-
-template <int D>
-struct MergeLds {
-  float m[kWavesPerBlock][kMaxGroup];
-  float l[kWavesPerBlock][kMaxGroup];
-  union {
-    float acc[kWavesPerBlock][kMaxGroup][D];
-    float w[kCombineChunk][kMaxGroup];  // final merge: weights of a chunk of partials
-  };
-  float head_m[kMaxGroup];
-  float head_inv_l[kMaxGroup];
-  uint32_t status[kWavesPerBlock];
-  uint32_t flag;
-};
-static_assert(sizeof(float) * kWavesPerBlock * kMaxGroup * 64 >= sizeof(float) * kCombineChunk * kMaxGroup,
-              "combine weights must fit in the merge buffer");
 
 // ------------------------------------------------------------------------
 // Geometry of one element type / head size.
@@ -519,7 +501,7 @@ __device__ __forceinline__ void valu_softmax_pv(ValuTile<KV, D>& t, ValuState<KV
 }
 
 // ------------------------------------------------------------------------
-// One wave: walk its tiles (every 4th tile of the block's chunk), checking
+// One wave: walk its consecutive tiles of one (sequence, KV head), checking
 // the pages of each round before any of their contents are used.
 // ------------------------------------------------------------------------
 template <int KV, int D, int GM, bool MFMA>
@@ -598,7 +580,7 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
     const int rt = min(round_tiles, n_wave_tiles - r0);
     // lane j -> wave page j of this round
     const int jt = lane >> ppt_log2;
-    const int tile_j = first_tile + 4 * (r0 + jt);
+    const int tile_j = first_tile + (r0 + jt);
     const int lp = log2ps < 6 ? (tile_j << ppt_log2) + (lane & ((1 << ppt_log2) - 1)) : (tile_j << 6) >> log2ps;
     const bool used = jt < rt && lp < n_pages_b;
     int pid = used ? p.page_table[pt_row + lp] : 0;
@@ -622,9 +604,9 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
     const uint8_t *kp, *vp;
     if (go) {
       // Speculative: page ids are range-checked; data is not used before the tag ballot.
-      tile_pointers<KV, D, GM, MFMA>(p, pr, 0, first_tile + 4 * r0, g, lane, kp, vp);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, 0, first_tile + r0, g, lane, kp, vp);
       load_tile<KV, D, GM, MFMA>(ta, kp, vp);
-      if constexpr (kVlds) v_tile_to_lds<D>(p, pr, 0, first_tile + 4 * r0, g, lane, vstage);
+      if constexpr (kVlds) v_tile_to_lds<D>(p, pr, 0, first_tile + r0, g, lane, vstage);
     }
     const bool any_mismatch = __any(actual != expected);
     status |= (any_bad ? kAbortMeta : 0u) | (any_mismatch ? kAbortTag : 0u);
@@ -643,16 +625,16 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
       const float sl = p.qk_scale_log2;
       v2i_t vt[2][Geo<0, D>::NB];
       for (int i = 0; i < rt; ++i) {
-        const int t0 = first_tile + 4 * (r0 + i);
+        const int t0 = first_tile + (r0 + i);
         const int n1 = min(i + 1, rt - 1);
         v_tile_from_lds<D>(vstage, lane, vt);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): tile i is out of LDS before it is overwritten
         __builtin_amdgcn_sched_barrier(0);
-        v_tile_to_lds<D>(p, pr, n1, first_tile + 4 * (r0 + n1), g, lane, vstage);
+        v_tile_to_lds<D>(p, pr, n1, first_tile + (r0 + n1), g, lane, vstage);
         f32x4_t sc[4];
         mfma_qk<KV, D>(ta, st, sc);
         __builtin_amdgcn_sched_barrier(0);
-        tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + 4 * (r0 + n1), g, lane, kp, vp);
+        tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + (r0 + n1), g, lane, kp, vp);
         mfma_load_k<KV, D>(ta, kp);
         mfma_softmax_pv_lds<D>(st, sc, vt, min(L - (t0 << 6), kTileTokens), sl, lane);
       }
@@ -665,15 +647,15 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
     const float sl = p.qk_scale_log2;
     for (int i = 0; i < rt; i += 2) {
       const int n1 = min(i + 1, rt - 1);
-      tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + 4 * (r0 + n1), g, lane, kp, vp);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + (r0 + n1), g, lane, kp, vp);
       load_tile<KV, D, GM, MFMA>(tb, kp, vp);
-      const int t0 = first_tile + 4 * (r0 + i);
+      const int t0 = first_tile + (r0 + i);
       compute_tile<KV, D, GM, MFMA>(ta, st, min(L - (t0 << 6), kTileTokens), sl, lane);
       if (i + 1 >= rt) break;
       const int n2 = min(i + 2, rt - 1);
-      tile_pointers<KV, D, GM, MFMA>(p, pr, n2, first_tile + 4 * (r0 + n2), g, lane, kp, vp);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, n2, first_tile + (r0 + n2), g, lane, kp, vp);
       load_tile<KV, D, GM, MFMA>(ta, kp, vp);
-      compute_tile<KV, D, GM, MFMA>(tb, st, min(L - ((t0 + 4) << 6), kTileTokens), sl, lane);
+      compute_tile<KV, D, GM, MFMA>(tb, st, min(L - ((t0 + 1) << 6), kTileTokens), sl, lane);
     }
     }
   }
@@ -681,35 +663,68 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
 }
 
 // ------------------------------------------------------------------------
-// Wave state -> LDS in the common layout m[w][h], l[w][h], acc[w][h][d].
+// Leaving a piece: a wave's state -> output rows or a published partial.
+//
+// MFMA family: lane l owns head l%16 and, for accumulator block nb and row
+// r, head-dim index acc_dim(nb, r, l); its running sum l is split over the 4
+// lane groups.  VALU family: after a merge across token slots, lanes 0..7
+// own dims [8*lane .. ) of every head.
 // ------------------------------------------------------------------------
 template <int KV, int D>
-__device__ __forceinline__ void export_state(MfmaState<KV, D>& st, MergeLds<D>& lds, int wave, int lane, int G) {
-  using G_ = Geo<KV, D>;
+__device__ __forceinline__ int acc_dim(int nb, int r, int lane) {
+  // FP8 (V^T read from LDS): dim 16*nb + 4*(lane/16) + r
+  // BF16 (V^T built in registers): dim NB*(4*(lane/16) + r) + nb
+  return KV == 0 ? 16 * nb + 4 * (lane >> 4) + r : Geo<KV, D>::NB * (4 * (lane >> 4) + r) + nb;
+}
+
+__device__ __forceinline__ void store_bf16(uint16_t* dst, float x) { *dst = (uint16_t)f32_to_bf16_bits(x); }
+
+template <int KV, int D>
+__device__ __forceinline__ void wave_output(MfmaState<KV, D>& st, const DecodeParams& p, int64_t out_row0, int lane) {
   float l = xor_sum(st.l, 16);
   l = xor_sum(l, 32);
   const int h = lane & 15;
-  if (h < G) {
+  if (h < p.group) {
+    const float inv = p.v_scale / l;
+    uint16_t* row = p.out + out_row0 + (int64_t)h * D;
 #pragma unroll
-    for (int nb = 0; nb < G_::NB; ++nb)
+    for (int nb = 0; nb < Geo<KV, D>::NB; ++nb) {
+      if constexpr (KV == 0) {  // 4 consecutive dims: one 8-byte store
+        u32x2_t w = {f32_to_bf16_bits(st.acc[nb][0] * inv) | (f32_to_bf16_bits(st.acc[nb][1] * inv) << 16),
+                     f32_to_bf16_bits(st.acc[nb][2] * inv) | (f32_to_bf16_bits(st.acc[nb][3] * inv) << 16)};
+        *reinterpret_cast<u32x2_t*>(row + acc_dim<KV, D>(nb, 0, lane)) = w;
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // FP8 (V^T read from LDS): row = dim 16*nb + 4*(lane/16) + r;
-        // BF16 (V^T built in registers): row = dim NB*(4*(lane/16) + r) + nb
-        const int d = KV == 0 ? 16 * nb + 4 * (lane >> 4) + r : G_::NB * (4 * (lane >> 4) + r) + nb;
-        lds.acc[wave][h][d] = st.acc[nb][r];
+        for (int r = 0; r < 4; ++r) store_bf16(row + acc_dim<KV, D>(nb, r, lane), st.acc[nb][r] * inv);
       }
-    if (lane < 16) {
-      lds.m[wave][h] = st.m;
-      lds.l[wave][h] = l;
     }
   }
 }
 
+template <int KV, int D>
+__device__ __forceinline__ void wave_publish(MfmaState<KV, D>& st, const DecodeParams& p, int64_t slot, int lane) {
+  float l = xor_sum(st.l, 16);
+  l = xor_sum(l, 32);
+  const int h = lane & 15;
+  const int G = p.group;
+  if (h < G) {
+    float* acc = p.part_acc + (slot * G + h) * D;
+#pragma unroll
+    for (int nb = 0; nb < Geo<KV, D>::NB; ++nb) {
+      if constexpr (KV == 0) {  // rows r = 0..3 are 4 consecutive dims
+        *reinterpret_cast<f32x4_t*>(acc + acc_dim<KV, D>(nb, 0, lane)) = st.acc[nb];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[acc_dim<KV, D>(nb, r, lane)] = st.acc[nb][r];
+      }
+    }
+    if (lane < 16) *reinterpret_cast<f32x2_t*>(p.part_ml + (slot * G + h) * 2) = f32x2_t{st.m, l};
+  }
+}
+
+// VALU family: merge the 8 token slots (lanes differing in bits 3..5) first.
 template <int KV, int D, int GM>
-__device__ __forceinline__ void export_state(ValuState<KV, D, GM>& st, MergeLds<D>& lds, int wave, int lane,
-                                             int G) {
-  constexpr int DC = Geo<KV, D>::DC;
+__device__ __forceinline__ void valu_merge_slots(ValuState<KV, D, GM>& st) {
 #pragma unroll
   for (int h = 0; h < GM; ++h) {
     float M = xor_max(st.m[h], 8);
@@ -719,18 +734,55 @@ __device__ __forceinline__ void export_state(ValuState<KV, D, GM>& st, MergeLds<
     float l = st.l[h] * w;
     l = xor_sum(l, 8);
     l = xor_sum(l, 16);
-    l = xor_sum(l, 32);
+    st.l[h] = xor_sum(l, 32);
+    st.m[h] = M;
 #pragma unroll
-    for (int i = 0; i < DC; ++i) {
+    for (int i = 0; i < Geo<KV, D>::DC; ++i) {
       float a = st.acc[h][i] * w;
       a = xor_sum(a, 8);
       a = xor_sum(a, 16);
-      a = xor_sum(a, 32);
-      if (lane < 8 && h < G) lds.acc[wave][h][(lane & 7) * DC + i] = a;
+      st.acc[h][i] = xor_sum(a, 32);
     }
-    if (lane == 0 && h < G) {
-      lds.m[wave][h] = M;
-      lds.l[wave][h] = l;
+  }
+}
+
+template <int KV, int D, int GM>
+__device__ __forceinline__ void wave_output(ValuState<KV, D, GM>& st, const DecodeParams& p, int64_t out_row0,
+                                            int lane) {
+  constexpr int DC = Geo<KV, D>::DC;
+  valu_merge_slots(st);
+  if (lane < 8) {
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      if (h < p.group) {
+        const float inv = p.v_scale / st.l[h];
+        uint16_t* row = p.out + out_row0 + (int64_t)h * D + lane * DC;
+#pragma unroll
+        for (int i = 0; i < DC; i += 2)
+          *reinterpret_cast<uint32_t*>(row + i) =
+              f32_to_bf16_bits(st.acc[h][i] * inv) | (f32_to_bf16_bits(st.acc[h][i + 1] * inv) << 16);
+      }
+    }
+  }
+}
+
+template <int KV, int D, int GM>
+__device__ __forceinline__ void wave_publish(ValuState<KV, D, GM>& st, const DecodeParams& p, int64_t slot,
+                                             int lane) {
+  constexpr int DC = Geo<KV, D>::DC;
+  valu_merge_slots(st);
+  const int G = p.group;
+  if (lane < 8) {
+#pragma unroll
+    for (int h = 0; h < GM; ++h) {
+      if (h < G) {
+        float* acc = p.part_acc + (slot * G + h) * D + lane * DC;
+#pragma unroll
+        for (int i = 0; i < DC; i += 4)
+          *reinterpret_cast<f32x4_t*>(acc + i) = f32x4_t{st.acc[h][i], st.acc[h][i + 1], st.acc[h][i + 2],
+                                                         st.acc[h][i + 3]};
+        if (lane == 0) *reinterpret_cast<f32x2_t*>(p.part_ml + (slot * G + h) * 2) = f32x2_t{st.m[h], st.l[h]};
+      }
     }
   }
 }
@@ -741,86 +793,56 @@ __device__ __forceinline__ void export_state(ValuState<KV, D, GM>& st, MergeLds<
 // All work of one call is the flattened list of (sequence b, KV head g,
 // tile t) triples, ordered b-major, then g, then t; sequence b contributes
 // num_kv_heads segments of T_b = ceil(L_b / 64) tiles (0 for a sequence
-// whose length is invalid).  Block k of nb takes the index range
-// [k*TT/nb, (k+1)*TT/nb) of the TT triples, so every block streams the same
-// number of tiles (+-1) whatever the length mix.  Each block derives the
-// schedule itself from seq_lens; the host never reads device memory.
+// whose length is invalid).  Wave w of the W = min(4 * num_blocks, TT) waves
+// takes the contiguous index range [w*TT/W, (w+1)*TT/W), so every wave
+// streams the same number of tiles (+-1) whatever the length mix.  Each wave
+// derives the schedule itself from seq_lens; the host never reads device
+// memory, and waves never wait for one another.
 //
-// A block's range is cut into pieces, one per segment it touches.  A piece
-// that is a whole segment is finished in place.  Otherwise only the first
-// and the last piece of a block can be partial: the first is stored in the
-// block's partial slot 0 (it starts at the range start), the last in slot 1.
-// The block that arrives last for a segment (arrival counter per (b, g))
-// merges the partials of blocks block_of(seg_lo) .. block_of(seg_hi - 1).
+// A wave's range is cut into pieces, one per segment it touches.  A piece
+// that is a whole segment is finished in registers.  Otherwise only the
+// first and the last piece of a wave can be partial: the first is published
+// in the wave's partial slot 0 (it starts at the range start), the last in
+// slot 1.  A second kernel (one block per segment) merges the partials of
+// waves wave_of(seg_lo) .. wave_of(seg_hi - 1); the kernel boundary makes
+// the partials visible to it, so no wave ever synchronizes with another.
 // ------------------------------------------------------------------------
-__device__ __forceinline__ int64_t range_start(int64_t k, int64_t total, int64_t nb) { return k * total / nb; }
-// the block whose range holds flattened index x
-__device__ __forceinline__ int64_t block_of(int64_t x, int64_t total, int64_t nb) { return ((x + 1) * nb - 1) / total; }
-
-struct ScanLds {
-  int64_t v[kBlockThreads];
-  int32_t tiles[kBlockThreads];
-  int64_t excl[kBlockThreads];
-  int32_t lo, hi;
-};
-
-// Inclusive scan of one int64 per thread over the block (Hillis-Steele in
-// LDS); `total` receives the block-wide sum.
-__device__ __forceinline__ int64_t block_inclusive_scan(int64_t x, ScanLds& sl, int tid, int64_t& total) {
-  sl.v[tid] = x;
-  __syncthreads();
-#pragma unroll
-  for (int off = 1; off < kBlockThreads; off <<= 1) {
-    const int64_t t = tid >= off ? sl.v[tid - off] : 0;
-    __syncthreads();
-    sl.v[tid] += t;
-    __syncthreads();
-  }
-  const int64_t r = sl.v[tid];
-  total = sl.v[kBlockThreads - 1];
-  __syncthreads();
-  return r;
-}
+__device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nw) { return w * total / nw; }
+// the wave whose range holds flattened index x
+__device__ __forceinline__ int64_t wave_of(int64_t x, int64_t total, int64_t nw) { return ((x + 1) * nw - 1) / total; }
 
 __device__ __forceinline__ int seq_tiles(int L, int max_tokens) {
   return (L >= 1 && L <= max_tokens) ? (L + kTileTokens - 1) / kTileTokens : 0;
 }
 
-// Merge the 4 waves' states of one (h, d-pair) element group.
-template <int D>
-__device__ __forceinline__ void merge_waves(const MergeLds<D>& lds, int h, int d, float& M, float& Ls, float& a0,
-                                            float& a1) {
-  M = kNegInf;
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
 #pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) M = __builtin_fmaxf(M, lds.m[w][h]);
-  Ls = 0.f;
-  a0 = 0.f;
-  a1 = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) {
-    const float wt = lds.m[w][h] == kNegInf ? 0.f : fast_exp2(lds.m[w][h] - M);
-    Ls += lds.l[w][h] * wt;
-    a0 += lds.acc[w][h][d] * wt;
-    a1 += lds.acc[w][h][d + 1] * wt;
-  }
+  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
-__device__ __forceinline__ void store_bf16_pair(uint16_t* dst, float a0, float a1) {
-  *reinterpret_cast<uint32_t*>(dst) = f32_to_bf16_bits(a0) | (f32_to_bf16_bits(a1) << 16);
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int64_t t = __shfl_up(v, off);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int64_t readlane64(int64_t v, int i) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, i);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), i);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // One piece: tiles [t_lo, t_hi) of segment (b, g), whose flattened range is
-// [seg_lo, seg_lo + T).  Ends with a block barrier (LDS is reused next).
+// [seg_lo, seg_lo + T).
 template <int KV, int D, int GM, bool MFMA>
-__device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>& lds, uint8_t* vstage, int b, int g,
-                                              int L, int T, int t_lo, int t_hi, int64_t seg_lo, int64_t r0,
-                                              int64_t TT, int64_t nb, int k, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ void wave_piece(const DecodeParams& p, uint8_t* vstage, int b, int g, int L, int T, int t_lo,
+                                           int t_hi, int64_t seg_lo, int64_t r0, int64_t w, int64_t TT, int64_t nw,
+                                           int lane) {
   const int G = p.group;
-  const int count = t_hi - t_lo;
-  const int n_wave_tiles = count > wave ? (count - wave + kWavesPerBlock - 1) / kWavesPerBlock : 0;
-
-  // ---- this wave's query operand and initial state
   typename WaveState<KV, D, GM, MFMA>::T st;
   const uint16_t* qrow0 = p.q + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
   if constexpr (MFMA) {
@@ -829,9 +851,9 @@ __device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>
     const int quarter = lane >> 4;
 #pragma unroll
     for (int kk = 0; kk < G_::KSTEPS; ++kk) {
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (col < G) w = *reinterpret_cast<const u32x4_t*>(qrow0 + (int64_t)col * D + quarter * (D / 4) + 8 * kk);
-      st.q[kk] = __builtin_bit_cast(bf16x8_t, w);
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (col < G) v = *reinterpret_cast<const u32x4_t*>(qrow0 + (int64_t)col * D + quarter * (D / 4) + 8 * kk);
+      st.q[kk] = __builtin_bit_cast(bf16x8_t, v);
     }
     st.m = kNegInf;
     st.l = 0.f;
@@ -842,15 +864,15 @@ __device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>
     const int dc = lane & 7;
 #pragma unroll
     for (int h = 0; h < GM; ++h) {
-      uint32_t w[DC / 2];
+      uint32_t v[DC / 2];
       if (h < G) {
-        load_words<DC / 2>(reinterpret_cast<const uint8_t*>(qrow0 + (int64_t)h * D + dc * DC), w);
+        load_words<DC / 2>(reinterpret_cast<const uint8_t*>(qrow0 + (int64_t)h * D + dc * DC), v);
       } else {
 #pragma unroll
-        for (int i = 0; i < DC / 2; ++i) w[i] = 0u;
+        for (int i = 0; i < DC / 2; ++i) v[i] = 0u;
       }
 #pragma unroll
-      for (int i = 0; i < DC / 2; ++i) st.q2[h][i] = w[i];
+      for (int i = 0; i < DC / 2; ++i) st.q2[h][i] = v[i];
       st.m[h] = kNegInf;
       st.l[h] = 0.f;
 #pragma unroll
@@ -858,87 +880,133 @@ __device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>
     }
   }
 
-  const uint32_t wave_status = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo + wave, n_wave_tiles, st, lane, vstage);
-  export_state(st, lds, wave, lane, G);
-  if (lane == 0) lds.status[wave] = wave_status;
-  __syncthreads();
-
-  uint32_t status = 0;
-#pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) status |= lds.status[w];
+  const uint32_t status = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo, t_hi - t_lo, st, lane, vstage);
   const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
-  const float v_scale = p.v_scale;
 
+  const int64_t seg = (int64_t)b * p.num_kv_heads + g;
   if (t_lo == 0 && t_hi == T) {
     // The whole segment is here: finish it.
-    if (tid == 0) p.abort_flags[b] = (uint8_t)status;
-    if (status == 0) {
-      for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
-        const int h = e / D, d = e - h * D;
-        float M, Ls, a0, a1;
-        merge_waves(lds, h, d, M, Ls, a0, a1);
-        const float inv = v_scale / Ls;
-        store_bf16_pair(p.out + out_row0 + e, a0 * inv, a1 * inv);
+    if (lane == 0) {
+      p.abort_flags[b] = (uint8_t)status;
+      p.seg_desc[seg] = 0;
+    }
+    if (status == 0) wave_output(st, p, out_row0, lane);
+    return;
+  }
+  if (t_lo == 0 && lane == 0) {
+    // The wave holding the segment's first tile tells the merge kernel
+    // where the segment's partials are: first slot, number of partials.
+    const uint32_t first_slot = (uint32_t)(2 * w + (r0 < seg_lo ? 1 : 0));
+    const uint32_t n_part = (uint32_t)(wave_of(seg_lo + T - 1, TT, nw) - w + 1);
+    p.seg_desc[seg] = first_slot | ((uint64_t)n_part << 32);
+  }
+
+  // A partial piece: publish it; the merge kernel combines the partials.
+  const int64_t slot = 2 * w + ((seg_lo + t_lo) == r0 ? 0 : 1);
+  if (status == 0) wave_publish(st, p, slot, lane);
+  if (lane == 0) p.part_status[slot] = status;
+}
+
+// ------------------------------------------------------------------------
+// The kernel: 4 independent waves per block, each with an equal share.
+// ------------------------------------------------------------------------
+template <int KV, int D, int GM, bool MFMA>
+__global__ __launch_bounds__(kBlockThreads, (MFMA && KV == 0) ? 2 : 1) void decode_kernel(DecodeParams p) {
+  // FP8 MFMA family: one 64-token V tile per wave staged in LDS
+  constexpr int kStage = (MFMA && KV == 0) ? kTileTokens * D : 16;
+  __shared__ __attribute__((aligned(16))) uint8_t vstage_all[kWavesPerBlock][kStage];
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  uint8_t* vstage = vstage_all[threadIdx.x >> 6];
+  const int max_tokens = p.max_pages << p.log2_page_size;
+  const int64_t hkv = p.num_kv_heads;
+
+  // ---- pass 1: total work; wave 0 flags sequences with unusable lengths
+  int64_t mine = 0;
+  for (int b = lane; b < p.batch; b += 64) {
+    const int T = seq_tiles(p.seq_lens[b], max_tokens);
+    mine += T;
+    if (T == 0 && w == 0) {
+      p.abort_flags[b] = (uint8_t)kAbortMeta;
+      for (int g = 0; g < p.num_kv_heads; ++g) p.seg_desc[(int64_t)b * p.num_kv_heads + g] = 0;
+    }
+  }
+  const int64_t TT = wave_sum64(mine) * hkv;
+  // Never more shares than tiles: every participating wave then owns at
+  // least one tile, so every wave inside a segment's span arrives.
+  const int64_t nw = min((int64_t)p.num_blocks * kWavesPerBlock, TT);
+  if (w >= nw) return;
+  const int64_t r0 = range_start(w, TT, nw), r1 = range_start(w + 1, TT, nw);
+
+  // ---- pass 2: walk the sequences 64 at a time, process the pieces in [r0, r1)
+  int64_t carry = 0;  // tiles per KV head of all sequences before this chunk
+  for (int c = 0; c < p.batch; c += 64) {
+    if (carry * hkv >= r1) break;
+    const int b = c + lane;
+    const int T = b < p.batch ? seq_tiles(p.seq_lens[b], max_tokens) : 0;
+    const int64_t incl = wave_inclusive_scan64(T, lane);
+    const int64_t excl = carry + incl - T;
+    const bool hit = T > 0 && excl * hkv < r1 && (excl + T) * hkv > r0;
+    uint64_t mask = __ballot(hit);
+    while (mask) {
+      const int i = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const int Ti = __builtin_amdgcn_readlane(T, i);
+      const int bi = c + i;
+      const int64_t seq_lo = readlane64(excl, i) * hkv;
+      const int L = p.seq_lens[bi];
+      const int64_t g_first = r0 > seq_lo ? (r0 - seq_lo) / Ti : 0;
+      const int64_t g_last = min(hkv - 1, (r1 - 1 - seq_lo) / Ti);
+      for (int64_t g = g_first; g <= g_last; ++g) {
+        const int64_t seg_lo = seq_lo + g * Ti;
+        const int t_lo = (int)(max(seg_lo, r0) - seg_lo);
+        const int t_hi = (int)(min(seg_lo + Ti, r1) - seg_lo);
+        wave_piece<KV, D, GM, MFMA>(p, vstage, bi, (int)g, L, Ti, t_lo, t_hi, seg_lo, r0, w, TT, nw, lane);
       }
     }
-    __syncthreads();
-    return;
+    carry += readlane64(incl, 63);
   }
+}
 
-  // ---- a partial piece: publish it
-  const int64_t slot = 2 * (int64_t)k + ((seg_lo + t_lo) == r0 ? 0 : 1);
-  if (status == 0) {
-    for (int e = 2 * tid; e < G * D; e += 2 * kBlockThreads) {
-      const int h = e / D, d = e - h * D;
-      float M, Ls, a0, a1;
-      merge_waves(lds, h, d, M, Ls, a0, a1);
-      *reinterpret_cast<f32x2_t*>(p.part_acc + (slot * G + h) * D + d) = f32x2_t{a0, a1};
-      if (d == 0) *reinterpret_cast<f32x2_t*>(p.part_ml + (slot * G + h) * 2) = f32x2_t{M, Ls};
-    }
-  }
-  if (tid == 0) p.part_status[slot] = status;
+// ------------------------------------------------------------------------
+// The merge kernel: one block of 256 threads per (sequence, KV head).
+// Segments finished inside one wave were written by the decode kernel; for
+// the others, OR the partials' abort bits, then combine the partials by
+// log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M), o = v_scale * sum
+// acc_a 2^(m_a - M) / L, rounded to BF16.
+// ------------------------------------------------------------------------
+constexpr int kMergeChunk = 256;  // partials whose weights are staged in LDS at a time
 
-  // Release the partial device-wide, then count arrivals for this segment.
-  const int64_t pair = (int64_t)b * p.num_kv_heads + g;
-  const int64_t first = block_of(seg_lo, TT, nb);
-  const int n_arr = (int)(block_of(seg_lo + T - 1, TT, nb) - first + 1);
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev = __hip_atomic_fetch_add(p.counters + pair, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    lds.flag = prev == (uint32_t)(n_arr - 1);
-  }
-  __syncthreads();
-  if (!lds.flag) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // ---- last arrival: merge the partials of blocks first .. first + n_arr - 1
-  const int64_t first_slot = 2 * first + (range_start(first, TT, nb) < seg_lo ? 1 : 0);
+template <int D>
+__global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
+  __shared__ float wts[kMergeChunk][kMaxGroup];
+  __shared__ float head_m[kMaxGroup], head_inv_l[kMaxGroup];
+  __shared__ uint32_t bits_sh;
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x;
+  const int b = (int)(seg / p.num_kv_heads), g = (int)(seg - (int64_t)b * p.num_kv_heads);
+  const int G = p.group;
+  const uint64_t desc = p.seg_desc[seg];
+  const int n_arr = (int)(desc >> 32);
+  if (n_arr < 2) return;  // finished inside one wave, or an unusable length
+  const int64_t first_slot = (uint32_t)desc;
+  const int64_t first = first_slot >> 1;
+  // a descriptor always names slots of this call's waves; never read past them
+  if (2 * (first + n_arr) > 2 * (int64_t)p.num_blocks * kWavesPerBlock) return;
   auto slot_of = [&](int a) -> int64_t { return a == 0 ? first_slot : 2 * (first + a); };
-  uint32_t st_all = 0;
-  for (int a = tid; a < n_arr; a += kBlockThreads) st_all |= p.part_status[slot_of(a)];
-  const bool any_bad = __ballot(st_all != 0) != 0;
-  __syncthreads();  // lds.status is rewritten below
-  if (lane == 0) lds.status[wave] = any_bad ? 1u : 0u;
+
+  if (tid == 0) bits_sh = 0;
   __syncthreads();
-  bool aborted = false;
-#pragma unroll
-  for (int w = 0; w < kWavesPerBlock; ++w) aborted |= lds.status[w] != 0;
-  if (aborted) {
-    if (tid == 0) {
-      uint32_t bits = 0;
-      for (int a = 0; a < n_arr; ++a) bits |= p.part_status[slot_of(a)];
-      p.abort_flags[b] = (uint8_t)bits;
-      p.counters[pair] = 0u;
-    }
-    __syncthreads();
-    return;
-  }
-  if (tid == 0) {
-    p.abort_flags[b] = 0;
-    p.counters[pair] = 0u;
-  }
-  // per head: M = max over partials, 1/L
+  uint32_t bits = 0;
+  for (int a = tid; a < n_arr; a += kBlockThreads) bits |= p.part_status[slot_of(a)];
+  if (bits) atomicOr(&bits_sh, bits);
+  __syncthreads();
+  bits = bits_sh;
+  if (tid == 0) p.abort_flags[b] = (uint8_t)bits;
+  if (bits != 0) return;
+
+  // per head: M and 1/L (one wave per head, lanes over partials)
+  const int lane = tid & 63, wave = tid >> 6;
   for (int h = wave; h < G; h += kWavesPerBlock) {
     float M = kNegInf;
     for (int a = lane; a < n_arr; a += 64) M = __builtin_fmaxf(M, p.part_ml[(slot_of(a) * G + h) * 2]);
@@ -952,129 +1020,55 @@ __device__ __forceinline__ void process_piece(const DecodeParams& p, MergeLds<D>
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) Ls = xor_sum(Ls, off);
     if (lane == 0) {
-      lds.head_m[h] = M;
-      lds.head_inv_l[h] = v_scale / Ls;
+      head_m[h] = M;
+      head_inv_l[h] = p.v_scale / Ls;
     }
   }
   __syncthreads();
-  float acc0[(kMaxGroup * D) / (2 * kBlockThreads)], acc1[(kMaxGroup * D) / (2 * kBlockThreads)];
+  // each thread: 4 consecutive dims of one head (G*D/4 <= 512 groups -> <= 2 per thread)
+  constexpr int PER = (kMaxGroup * D / 4 + kBlockThreads - 1) / kBlockThreads;
+  f32x4_t acc[PER];
 #pragma unroll
-  for (int i = 0; i < (kMaxGroup * D) / (2 * kBlockThreads); ++i) acc0[i] = acc1[i] = 0.f;
-  for (int a0 = 0; a0 < n_arr; a0 += kCombineChunk) {
-    const int na = min(kCombineChunk, n_arr - a0);
+  for (int i = 0; i < PER; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int a0 = 0; a0 < n_arr; a0 += kMergeChunk) {
+    const int na = min(kMergeChunk, n_arr - a0);
     for (int e = tid; e < na * G; e += kBlockThreads) {
       const int a = e / G, h = e - a * G;
-      lds.w[a][h] = fast_exp2(p.part_ml[(slot_of(a0 + a) * G + h) * 2] - lds.head_m[h]);
+      wts[a][h] = fast_exp2(p.part_ml[(slot_of(a0 + a) * G + h) * 2] - head_m[h]);
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < (kMaxGroup * D) / (2 * kBlockThreads); ++i) {
-      const int e = 2 * tid + i * 2 * kBlockThreads;
+    for (int i = 0; i < PER; ++i) {
+      const int e = 4 * (tid + i * kBlockThreads);
       if (e < G * D) {
         const int h = e / D, d = e - h * D;
-        float x0 = acc0[i], x1 = acc1[i];
-        for (int a = 0; a < na; ++a) {
-          const f32x2_t av = *reinterpret_cast<const f32x2_t*>(p.part_acc + (slot_of(a0 + a) * G + h) * D + d);
-          const float wt = lds.w[a][h];
-          x0 += av[0] * wt;
-          x1 += av[1] * wt;
-        }
-        acc0[i] = x0;
-        acc1[i] = x1;
+        f32x4_t x = acc[i];
+        for (int a = 0; a < na; ++a)
+          x += *reinterpret_cast<const f32x4_t*>(p.part_acc + (slot_of(a0 + a) * G + h) * D + d) * wts[a][h];
+        acc[i] = x;
       }
     }
     __syncthreads();
   }
+  uint16_t* out = p.out + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
 #pragma unroll
-  for (int i = 0; i < (kMaxGroup * D) / (2 * kBlockThreads); ++i) {
-    const int e = 2 * tid + i * 2 * kBlockThreads;
+  for (int i = 0; i < PER; ++i) {
+    const int e = 4 * (tid + i * kBlockThreads);
     if (e < G * D) {
-      const int h = e / D;
-      const float inv = lds.head_inv_l[h];
-      store_bf16_pair(p.out + out_row0 + e, acc0[i] * inv, acc1[i] * inv);
+      const float inv = head_inv_l[e / D];
+      const u32x2_t v = {f32_to_bf16_bits(acc[i][0] * inv) | (f32_to_bf16_bits(acc[i][1] * inv) << 16),
+                         f32_to_bf16_bits(acc[i][2] * inv) | (f32_to_bf16_bits(acc[i][3] * inv) << 16)};
+      *reinterpret_cast<u32x2_t*>(out + e) = v;
     }
-  }
-  __syncthreads();
-}
-
-// ------------------------------------------------------------------------
-// The kernel: one block per share of the flattened work.
-// ------------------------------------------------------------------------
-template <int KV, int D, int GM, bool MFMA>
-__global__ __launch_bounds__(kBlockThreads, (MFMA && KV == 0) ? 2 : 1) void decode_kernel(DecodeParams p) {
-  __shared__ MergeLds<D> lds;
-  __shared__ ScanLds sl;
-  // FP8 MFMA family: one 64-token V tile per wave staged in LDS
-  constexpr int kStage = (MFMA && KV == 0) ? kTileTokens * D : 16;
-  __shared__ __attribute__((aligned(16))) uint8_t vstage_all[kWavesPerBlock][kStage];
-  const int tid = threadIdx.x;
-  const int k = blockIdx.x;
-  const int max_tokens = p.max_pages << p.log2_page_size;
-  const int64_t hkv = p.num_kv_heads;
-
-  // ---- pass 1: total work; block 0 flags sequences with unusable lengths
-  int64_t mine = 0;
-  for (int b = tid; b < p.batch; b += kBlockThreads) {
-    const int T = seq_tiles(p.seq_lens[b], max_tokens);
-    mine += T;
-    if (T == 0 && k == 0) p.abort_flags[b] = (uint8_t)kAbortMeta;
-  }
-  int64_t seq_total;
-  block_inclusive_scan(mine, sl, tid, seq_total);
-  const int64_t TT = seq_total * hkv;
-  // Never more shares than tiles: every participating block then owns at
-  // least one tile, so every block inside a segment's span arrives.
-  const int64_t nb = min((int64_t)p.num_blocks, TT);
-  if (k >= nb) return;
-  const int64_t r0 = range_start(k, TT, nb), r1 = range_start(k + 1, TT, nb);
-
-  // ---- pass 2: walk the sequences in chunks, process the pieces in [r0, r1)
-  int64_t carry = 0;  // tiles per KV head of all sequences before this chunk
-  for (int c = 0; c < p.batch; c += kBlockThreads) {
-    if (carry * hkv >= r1) break;
-    const int b = c + tid;
-    const int T = b < p.batch ? seq_tiles(p.seq_lens[b], max_tokens) : 0;
-    int64_t chunk_total;
-    const int64_t incl = block_inclusive_scan(T, sl, tid, chunk_total);
-    const int64_t excl = carry + incl - T;
-    sl.tiles[tid] = T;
-    sl.excl[tid] = excl;
-    if (tid == 0) {
-      sl.lo = kBlockThreads;
-      sl.hi = -1;
-    }
-    __syncthreads();
-    const bool hit = T > 0 && excl * hkv < r1 && (excl + T) * hkv > r0;
-    if (hit) {
-      atomicMin(&sl.lo, tid);
-      atomicMax(&sl.hi, tid);
-    }
-    __syncthreads();
-    const int lo = sl.lo, hi = sl.hi;
-    for (int i = lo; i <= hi; ++i) {
-      const int Ti = sl.tiles[i];
-      if (Ti == 0) continue;
-      const int bi = c + i;
-      const int64_t seq_lo = sl.excl[i] * hkv;
-      const int L = p.seq_lens[bi];
-      const int64_t g_first = r0 > seq_lo ? (r0 - seq_lo) / Ti : 0;
-      const int64_t g_last = min((int64_t)(hkv - 1), (r1 - 1 - seq_lo) / Ti);
-      for (int64_t g = g_first; g <= g_last; ++g) {
-        const int64_t seg_lo = seq_lo + g * Ti;
-        const int t_lo = (int)(max(seg_lo, r0) - seg_lo);
-        const int t_hi = (int)(min(seg_lo + Ti, r1) - seg_lo);
-        process_piece<KV, D, GM, MFMA>(p, lds, vstage_all[tid >> 6], bi, (int)g, L, Ti, t_lo, t_hi, seg_lo, r0, TT,
-                                       nb, k, tid);
-      }
-    }
-    carry += chunk_total;
-    __syncthreads();  // sl is rewritten by the next chunk
   }
 }
 
 template <int KV, int D, int GM, bool MFMA>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), dim3(p.num_blocks), dim3(kBlockThreads), 0, stream, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(p.batch * p.num_kv_heads)), dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
 }
 

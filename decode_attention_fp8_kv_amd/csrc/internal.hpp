@@ -9,7 +9,7 @@
 namespace fp8kv {
 
 constexpr int kTileTokens = 64;   // tokens per tile handled by one wave at a time
-constexpr int kWavesPerBlock = 4; // waves per workgroup; they split one chunk of tiles
+constexpr int kWavesPerBlock = 4; // waves per workgroup (independent workers)
 constexpr int kBlockThreads = 64 * kWavesPerBlock;
 constexpr int kMaxGroup = 16;     // query heads per KV head handled by one workgroup
 
@@ -35,23 +35,23 @@ struct DecodeParams {
   const uint32_t* expected_tags;    // [B][max_pages] or null
   uint16_t* out;                    // bf16 [B][Hq][D]
   uint8_t* abort_flags;             // [B]
-  uint32_t* counters;               // [B*Hkv] arrivals per (sequence, KV head); zero between calls
-  uint32_t* part_status;            // [2*num_blocks]        abort bits of each partial piece
-  float* part_ml;                   // [2*num_blocks][G][2]  running max (log2 domain), sum
-  float* part_acc;                  // [2*num_blocks][G][D]  unnormalized output
+  uint64_t* seg_desc;               // [B*Hkv] first partial slot | number of partials << 32 (< 2: none)
+  uint32_t* part_status;            // [2*waves]        abort bits of each partial piece
+  float* part_ml;                   // [2*waves][G][2]  running max (log2 domain), sum
+  float* part_acc;                  // [2*waves][G][D]  unnormalized output
   int32_t batch, num_q_heads, num_kv_heads, group, max_pages, num_pages;
   int32_t log2_page_size;
-  int32_t num_blocks;               // grid size; block k owns an equal share of all tiles
+  int32_t num_blocks;               // grid size; each of its 4*num_blocks waves owns an equal share
   float qk_scale_log2;              // softmax_scale * k_scale * log2(e)
   float v_scale;                    // folded into the final normalization
 };
 
 // Grid size chosen on the host from sizes only (no device reads).
 int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages,
-                    int32_t num_blocks);
+                    int32_t num_blocks, int32_t blocks_per_cu);
 
 struct WorkspaceLayout {
-  size_t counters, part_status, part_ml, part_acc, total;
+  size_t seg_desc, part_status, part_ml, part_acc, total;
 };
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t num_blocks);

@@ -157,10 +157,14 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *                  FP8KV_ABORT_* bits
  *   workspace      device buffer of at least
  *                  paged_decode_attn_workspace_size(...) bytes, 256-byte
- *                  aligned, ZERO-FILLED BEFORE ITS FIRST USE; every call
- *                  leaves its counters at zero again, so it can be reused
- *                  without clearing.  Calls sharing a workspace must be
- *                  ordered (same stream).
+ *                  aligned; its contents need no initialization (each call
+ *                  writes what it reads).  It holds per-call partial
+ *                  results, so calls sharing a workspace must be ordered
+ *                  (same stream).
+ *
+ * A call enqueues two kernels on the stream: the split decode kernel and a
+ * merge kernel that combines the partial results of sequences whose work
+ * was split between workgroups.
  *   num_blocks     0 = choose automatically; n > 0 = use n workgroups
  *                  (at most 65535).  The batch's work -- every (sequence,
  *                  KV head, 64-token tile) -- is cut into n equal contiguous

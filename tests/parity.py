@@ -94,6 +94,7 @@ def gpu_decode(w, kv_dtype, kc, vc, dev, tags_on=True, num_blocks=0, seq_lens=No
     flags = torch.full((w.batch,), 0xEE, dtype=torch.uint8, device=dev)
     ws = fk.alloc_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                             page_table.shape[1], num_blocks, device=dev)
+    ws.fill_(0xA5)  # the workspace needs no initialization: start from garbage
     tags = torch.from_numpy(page_tags.view(np.int32)).to(dev) if tags_on else None
     exp = torch.from_numpy(np.ascontiguousarray(expected_tags).view(np.int32)).to(dev) if tags_on else None
     fk.paged_decode_attn(w.q.to(dev).contiguous(), kc, vc, torch.from_numpy(page_table).to(dev),

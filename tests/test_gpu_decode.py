@@ -32,9 +32,6 @@ def _run_case(w, kv_dtype, dev, tags_on=True, num_blocks=0, **over):
     ref, rflags = oracle_decode(w, kv_dtype, okc, ovc, tags_on=tags_on, **over)
     assert np.array_equal(flags, rflags), f"abort flags {flags} != oracle {rflags}"
     compare_outputs(out, ref, flags)
-    # every arrival counter is back at zero, ready for the next call
-    n_pairs = w.batch * w.num_kv_heads
-    assert int(ws[:4 * n_pairs].count_nonzero()) == 0
     return out, flags, (kc, vc)
 
 
