@@ -37,7 +37,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
 constexpr int64_t kComputeUnits = 256;    // MI355X; the default grid keeps every block resident
-constexpr int32_t kMaxBlocksPerCu = 2;
+constexpr int32_t kBlocksPerCu = 1;        // 4 waves per CU stream as fast as 8 and split the work less
 constexpr int64_t kMinTilesPerWave = 8;   // below this, fewer waves: merge cost beats parallelism
 constexpr int64_t kMaxBlocks = 65535;
 constexpr int64_t kMaxTotalTiles = int64_t(1) << 40;
@@ -142,7 +142,7 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int3
                                         int32_t page_size, int32_t max_pages, int32_t num_blocks) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_blocks < 0) return 0;
   if (num_q_heads % num_kv_heads != 0 || !supported_head_dim(head_dim) || log2_page_size(page_size) < 0) return 0;
-  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kMaxBlocksPerCu);
+  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kBlocksPerCu);
   return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb).total;
 }
 
@@ -182,8 +182,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
     return FP8KV_ERR_ALIGN;
   const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
   // resident blocks per CU: the FP8 MFMA kernel runs 2 waves per SIMD, the others 1
-  const int32_t per_cu = (mfma && kv_dtype == FP8KV_KV_FP8_E4M3) ? 2 : 1;
-  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, per_cu);
+  const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kBlocksPerCu);
   const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb);
   if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;
 

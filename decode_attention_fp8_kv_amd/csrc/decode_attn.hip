@@ -911,7 +911,7 @@ __device__ __forceinline__ void wave_piece(const DecodeParams& p, uint8_t* vstag
 // The kernel: 4 independent waves per block, each with an equal share.
 // ------------------------------------------------------------------------
 template <int KV, int D, int GM, bool MFMA>
-__global__ __launch_bounds__(kBlockThreads, (MFMA && KV == 0) ? 2 : 1) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p) {
   // FP8 MFMA family: one 64-token V tile per wave staged in LDS
   constexpr int kStage = (MFMA && KV == 0) ? kTileTokens * D : 16;
   __shared__ __attribute__((aligned(16))) uint8_t vstage_all[kWavesPerBlock][kStage];
