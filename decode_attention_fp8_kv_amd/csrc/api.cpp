@@ -164,7 +164,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_pages <= 0 || num_blocks < 0)
     return FP8KV_ERR_SHAPE;
   if (num_q_heads % num_kv_heads != 0) return FP8KV_ERR_SHAPE;
-  if (batch > 65535 || num_kv_heads > 65535 || (int64_t)batch * num_kv_heads > INT32_MAX) return FP8KV_ERR_SHAPE;
+  if (batch > 65535 || num_kv_heads > 65535 || (int64_t)batch * num_q_heads > INT32_MAX) return FP8KV_ERR_SHAPE;
   const int32_t group = num_q_heads / num_kv_heads;
   if (group > kMaxGroup || !supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
   const int l2ps = log2_page_size(page_size);

@@ -969,23 +969,27 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 }
 
 // ------------------------------------------------------------------------
-// The merge kernel: one block of 256 threads per (sequence, KV head).
-// Segments finished inside one wave were written by the decode kernel; for
-// the others, OR the partials' abort bits, then combine the partials by
-// log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M), o = v_scale * sum
-// acc_a 2^(m_a - M) / L, rounded to BF16.
+// The merge kernel: one wave per (sequence, KV head, query head of the
+// group), four per block.  Segments finished inside one wave were written
+// by the decode kernel; for the others, OR the partials' abort bits, then
+// combine the partials by log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M),
+// o = v_scale * sum acc_a 2^(m_a - M) / L, rounded to BF16.  Lanes hold
+// the statistics of 64 partials at a time and the output dims of the head;
+// each partial's accumulator row is one coalesced load per wave, and
+// kMergeUnroll of them are in flight at once.
 // ------------------------------------------------------------------------
-constexpr int kMergeChunk = 256;  // partials whose weights are staged in LDS at a time
+constexpr int kMergeUnroll = 16;
 
 template <int D>
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
-  __shared__ float wts[kMergeChunk][kMaxGroup];
-  __shared__ float head_m[kMaxGroup], head_inv_l[kMaxGroup];
-  __shared__ uint32_t bits_sh;
-  const int tid = threadIdx.x;
-  const int64_t seg = blockIdx.x;
-  const int b = (int)(seg / p.num_kv_heads), g = (int)(seg - (int64_t)b * p.num_kv_heads);
+  constexpr int DL = D / 64;  // output dims per lane
+  const int lane = threadIdx.x & 63;
   const int G = p.group;
+  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  if (item >= (int64_t)p.batch * p.num_kv_heads * G) return;
+  const int64_t seg = item / G;
+  const int h = (int)(item - seg * G);
+  const int b = (int)(seg / p.num_kv_heads), g = (int)(seg - (int64_t)b * p.num_kv_heads);
   const uint64_t desc = p.seg_desc[seg];
   const int n_arr = (int)(desc >> 32);
   if (n_arr < 2) return;  // finished inside one wave, or an unusable length
@@ -995,71 +999,74 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   if (2 * (first + n_arr) > 2 * (int64_t)p.num_blocks * kWavesPerBlock) return;
   auto slot_of = [&](int a) -> int64_t { return a == 0 ? first_slot : 2 * (first + a); };
 
-  if (tid == 0) bits_sh = 0;
-  __syncthreads();
+  // abort bits and the maximum over all partials (lane a: partials a, a+64, ...)
   uint32_t bits = 0;
-  for (int a = tid; a < n_arr; a += kBlockThreads) bits |= p.part_status[slot_of(a)];
-  if (bits) atomicOr(&bits_sh, bits);
-  __syncthreads();
-  bits = bits_sh;
-  if (tid == 0) p.abort_flags[b] = (uint8_t)bits;
+  float M = kNegInf, m0 = kNegInf, l0 = 0.f;
+  for (int a = lane; a < n_arr; a += 64) {
+    const int64_t sl = slot_of(a);
+    bits |= p.part_status[sl];
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (sl * G + h) * 2);
+    if (a < 64) {
+      m0 = ml[0];
+      l0 = ml[1];
+    }
+    M = __builtin_fmaxf(M, ml[0]);
+  }
+  bits = (__any(bits & kAbortTag) ? kAbortTag : 0u) | (__any(bits & kAbortMeta) ? kAbortMeta : 0u);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) M = xor_max(M, off);
+  if (h == 0 && lane == 0) p.abort_flags[b] = (uint8_t)bits;
   if (bits != 0) return;
 
-  // per head: M and 1/L (one wave per head, lanes over partials)
-  const int lane = tid & 63, wave = tid >> 6;
-  for (int h = wave; h < G; h += kWavesPerBlock) {
-    float M = kNegInf;
-    for (int a = lane; a < n_arr; a += 64) M = __builtin_fmaxf(M, p.part_ml[(slot_of(a) * G + h) * 2]);
+  // 64 partials at a time: lane j's weight 2^(m - M) is read by every lane
+  float Ls = 0.f;
+  float x[DL];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) M = xor_max(M, off);
-    float Ls = 0.f;
-    for (int a = lane; a < n_arr; a += 64) {
-      const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (slot_of(a) * G + h) * 2);
-      Ls += ml[1] * fast_exp2(ml[0] - M);
+  for (int k = 0; k < DL; ++k) x[k] = 0.f;
+  const float* acc_h = p.part_acc + (int64_t)h * D + lane * DL;
+  for (int a0 = 0; a0 < n_arr; a0 += 64) {
+    float m = m0, l = l0;
+    if (a0 > 0 && a0 + lane < n_arr) {
+      const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (slot_of(a0 + lane) * G + h) * 2);
+      m = ml[0];
+      l = ml[1];
     }
+    const float wgt = (a0 + lane < n_arr) ? fast_exp2(m - M) : 0.f;
+    Ls += l * wgt;
+    const int na = min(64, n_arr - a0);
+    for (int j0 = 0; j0 < na; j0 += kMergeUnroll) {
+      float v[kMergeUnroll][DL];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) Ls = xor_sum(Ls, off);
-    if (lane == 0) {
-      head_m[h] = M;
-      head_inv_l[h] = p.v_scale / Ls;
-    }
-  }
-  __syncthreads();
-  // each thread: 4 consecutive dims of one head (G*D/4 <= 512 groups -> <= 2 per thread)
-  constexpr int PER = (kMaxGroup * D / 4 + kBlockThreads - 1) / kBlockThreads;
-  f32x4_t acc[PER];
+      for (int j = 0; j < kMergeUnroll; ++j) {
+        const int jj = min(j0 + j, na - 1);  // past the end: re-read the last row, weight 0
+        const float* src = acc_h + slot_of(a0 + jj) * G * D;
+        if constexpr (DL == 2) {
+          const f32x2_t t = *reinterpret_cast<const f32x2_t*>(src);
+          v[j][0] = t[0];
+          v[j][1] = t[1];
+        } else {
+          v[j][0] = *src;
+        }
+      }
 #pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int a0 = 0; a0 < n_arr; a0 += kMergeChunk) {
-    const int na = min(kMergeChunk, n_arr - a0);
-    for (int e = tid; e < na * G; e += kBlockThreads) {
-      const int a = e / G, h = e - a * G;
-      wts[a][h] = fast_exp2(p.part_ml[(slot_of(a0 + a) * G + h) * 2] - head_m[h]);
-    }
-    __syncthreads();
+      for (int j = 0; j < kMergeUnroll; ++j) {
+        const int src_lane = min(j0 + j, 63);
+        const float wj = j0 + j < na ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                    __builtin_bit_cast(int, wgt), src_lane))
+                                     : 0.f;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int e = 4 * (tid + i * kBlockThreads);
-      if (e < G * D) {
-        const int h = e / D, d = e - h * D;
-        f32x4_t x = acc[i];
-        for (int a = 0; a < na; ++a)
-          x += *reinterpret_cast<const f32x4_t*>(p.part_acc + (slot_of(a0 + a) * G + h) * D + d) * wts[a][h];
-        acc[i] = x;
+        for (int k = 0; k < DL; ++k) x[k] += v[j][k] * wj;
       }
     }
-    __syncthreads();
   }
-  uint16_t* out = p.out + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = 4 * (tid + i * kBlockThreads);
-    if (e < G * D) {
-      const float inv = head_inv_l[e / D];
-      const u32x2_t v = {f32_to_bf16_bits(acc[i][0] * inv) | (f32_to_bf16_bits(acc[i][1] * inv) << 16),
-                         f32_to_bf16_bits(acc[i][2] * inv) | (f32_to_bf16_bits(acc[i][3] * inv) << 16)};
-      *reinterpret_cast<u32x2_t*>(out + e) = v;
-    }
+  for (int off = 1; off < 64; off <<= 1) Ls = xor_sum(Ls, off);
+  const float inv = p.v_scale / Ls;
+  uint16_t* out = p.out + ((int64_t)b * p.num_q_heads + (int64_t)g * G + h) * D + lane * DL;
+  if constexpr (DL == 2) {
+    *reinterpret_cast<uint32_t*>(out) = f32_to_bf16_bits(x[0] * inv) | (f32_to_bf16_bits(x[1] * inv) << 16);
+  } else {
+    *out = (uint16_t)f32_to_bf16_bits(x[0] * inv);
   }
 }
 
@@ -1068,7 +1075,9 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), dim3(p.num_blocks), dim3(kBlockThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(p.batch * p.num_kv_heads)), dim3(kBlockThreads), 0, stream, p);
+  const int64_t merge_waves = (int64_t)p.batch * p.num_kv_heads * p.group;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((merge_waves + kWavesPerBlock - 1) / kWavesPerBlock)),
+                     dim3(kBlockThreads), 0, stream, p);
   return hipGetLastError();
 }
 
