@@ -16,6 +16,7 @@ time from HIP events on the launch stream) and the CPU oracle's rate on a
 bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --summarize-profiles OUT   (writes profiles/ from rocprofv3 runs)
 """
 
 from __future__ import annotations
@@ -220,7 +221,104 @@ def cpu_baseline(w, budget_s=15.0):
     }
 
 
+PROFILE_TRACE = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_trace.md")
+PROFILE_CMDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o run -- "
+             "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pmc_fetch -o run -- "
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pmc_write -o run -- "
+             "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
+}
+COPY_BYTES = 2 << 30            # the device copy of copy_bandwidth(): the counters' calibration
+
+
+def summarize_profiles(out_dir: str) -> None:
+    """Write the committed text summaries from the three rocprofv3 runs in
+    PROFILE_CMDS (run from the repository root, OUT = out_dir).  The counter
+    pass reads FETCH_SIZE / WRITE_SIZE in KiB per dispatch; each is scaled by
+    bytes / counter of the 2 GiB device copy measured in the same run."""
+    import csv
+    from collections import defaultdict
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    stats = rows(os.path.join(out_dir, "trace", "run_kernel_stats.csv"))
+    keep = [r for r in stats if "fp8kv" in r["Name"]]
+    lines = ["# paged_decode_attn kernels on the conc32 workload (FP8 and BF16 KV): kernel trace", "",
+             "Command (from the repository root; OUT is any output folder):", "",
+             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["trace"], "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    avg = {}
+    for r in keep:
+        name = r["Name"].replace("void fp8kv::(anonymous namespace)::", "").replace("(fp8kv::DecodeParams)", "")
+        name = name.replace("(fp8kv::AppendParams)", "")
+        avg[name] = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{name}` | {r['Calls']} | {avg[name]:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    dec = avg.get("decode_kernel<0, 128, 16, true>")
+    mrg = avg.get("merge_kernel<128>")
+    if dec is not None and mrg is not None:
+        lines += ["", f"One FP8 `paged_decode_attn` call = decode_kernel<0, 128, 16, true> + merge_kernel<128> = "
+                      f"{dec:.2f} + {mrg:.2f} = {dec + mrg:.2f} us of kernel time (the merge kernel's average "
+                      f"covers the FP8 and BF16 calls).",
+                  "decode_kernel<0,...> is the FP8-cache instance, decode_kernel<1,...> the BF16 one; "
+                  "quant_append_kernel<0>/<1> are kv_quant_append (their averages include the one-off fill of "
+                  "the whole cache before timing)."]
+    lines.append("")
+    with open(PROFILE_TRACE, "w") as f:
+        f.write("\n".join(lines))
+
+    per = {}
+    for key, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        vals = defaultdict(list)
+        for r in rows(os.path.join(out_dir, f"pmc_{key}", "run_counter_collection.csv")):
+            if r["Counter_Name"] == counter:
+                vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        copy = [v for k, v in vals.items() if "copyBuffer" in k for v in v]
+        big = [v for v in copy if v >= 0.9 * max(copy)]
+        factor = COPY_BYTES / (sum(big) / len(big) * 1024.0)
+        dk = [v for k, v in vals.items() if "decode_kernel<0, 128, 16, true>" in k for v in v]
+        mk = [v for k, v in vals.items() if "merge_kernel<128>" in k for v in v]
+        per[key] = (factor, sum(dk) / len(dk), sum(mk) / len(mk), len(dk), len(big))
+    ff, fd, fm, nd, nc = per["fetch"]
+    wf, wd, wm, _, _ = per["write"]
+    traffic = (fd + fm) * 1024.0 * ff + (wd + wm) * 1024.0 * wf
+    from decode_attention_fp8_kv_amd import workloads as W
+    w = W.make(WORKLOAD)
+    alg = algorithmic_bytes(w, 0)
+    out = [
+        "# HBM traffic of one FP8 paged_decode_attn call (decode_kernel<0, 128, 16, true> + merge_kernel<128>)",
+        "# on the conc32 workload, from two rocprofv3 counter passes (from the repository root; OUT is any folder):",
+        "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
+        "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["write"],
+        "# Counters are KiB per dispatch; each is scaled by bytes / counter of the 2 GiB device copy",
+        "# (__amd_rocclr_copyBuffer) that bench.py runs in the same process.",
+        f"kernel_source_hash: {kernel_source_hash()}",
+        f"decode_dispatches: {nd}",
+        f"copy_dispatches: {nc}",
+        f"fetch_kib_per_dispatch_decode: {fd:.1f}",
+        f"fetch_kib_per_dispatch_merge: {fm:.1f}",
+        f"write_kib_per_dispatch_decode: {wd:.1f}",
+        f"write_kib_per_dispatch_merge: {wm:.1f}",
+        f"fetch_scale: {ff:.4f}",
+        f"write_scale: {wf:.4f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"algorithmic_bytes_per_launch: {alg}",
+        f"traffic_over_algorithmic: {traffic / alg:.4f}",
+        "",
+    ]
+    with open(PROFILE_COUNTERS, "w") as f:
+        f.write("\n".join(out))
+    print(f"wrote {PROFILE_TRACE} and {PROFILE_COUNTERS}")
+
+
 def main():
+    if len(sys.argv) == 3 and sys.argv[1] == "--summarize-profiles":
+        summarize_profiles(sys.argv[2])
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -305,7 +403,7 @@ def main():
         "decode_us": {"mean": round(f["decode_mean_us"], 2), "median": round(f["decode_median_us"], 2),
                       "p95": round(f["decode_p95_us"], 2)},
         "roofline": {
-            "kernel": "decode_kernel<fp8,128,16,mfma> (paged_decode_attn)",
+            "kernel": "paged_decode_attn FP8: decode_kernel<0,128,16,true> + merge_kernel<128>",
             "bound": "hbm",
             "achieved": round(f["gbps"], 1),
             "peak": PEAK_HBM_GBPS,
