@@ -120,8 +120,9 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new,
 
 /*
  * paged_decode_attn_workspace_size -- bytes of device workspace that
- * paged_decode_attn needs for these sizes (a multiple of 256; at most a few
- * MiB).  num_blocks has the meaning it has in paged_decode_attn.  Returns 0
+ * paged_decode_attn needs for these sizes (a multiple of 256; mostly
+ * 2 * 4 * num_blocks partial slots of 4 * G * (head_dim + 2) bytes each,
+ * G = num_q_heads / num_kv_heads: up to ~17 MiB with the automatic grid).  num_blocks has the meaning it has in paged_decode_attn.  Returns 0
  * if the sizes are invalid.
  */
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
@@ -165,12 +166,18 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  * A call enqueues two kernels on the stream: the split decode kernel and a
  * merge kernel that combines the partial results of sequences whose work
  * was split between workgroups.
- *   num_blocks     0 = choose automatically; n > 0 = use n workgroups
+ *   num_blocks     0 = choose automatically (one workgroup per CU, fewer
+ *                  for small batches); n > 0 = use n workgroups of 4 waves
  *                  (at most 65535).  The batch's work -- every (sequence,
- *                  KV head, 64-token tile) -- is cut into n equal contiguous
- *                  shares, so long sequences are split across workgroups
- *                  (flash-decoding) and merged exactly; the result does not
- *                  depend on n beyond floating-point rounding.
+ *                  KV head, 64-token tile) -- is cut into min(4n, tiles)
+ *                  equal contiguous shares, one per wave, so long sequences
+ *                  are split across waves (flash-decoding) and merged
+ *                  exactly; the result does not depend on n beyond
+ *                  floating-point rounding, and repeated calls with the same
+ *                  inputs and n give bit-identical outputs.
+ *
+ * A call enqueues two kernels on the stream: the decode kernel and a merge
+ * kernel that combines the partial results of segments split between waves.
  *
  * Tag rule: for every page slot j < ceil(L / page_size) (the partial last
  * page included), the page id p = page_table[b*max_pages + j] must lie in
