@@ -122,8 +122,9 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new,
  * paged_decode_attn_workspace_size -- bytes of device workspace that
  * paged_decode_attn needs for these sizes (a multiple of 256; mostly
  * 2 * 4 * num_blocks partial slots of 4 * G * (head_dim + 2) bytes each,
- * G = num_q_heads / num_kv_heads: up to ~17 MiB with the automatic grid).  num_blocks has the meaning it has in paged_decode_attn.  Returns 0
- * if the sizes are invalid.
+ * G = num_q_heads / num_kv_heads: up to ~17 MiB with the automatic grid).
+ * num_blocks has the meaning it has in paged_decode_attn.  Returns 0 if the
+ * sizes are invalid.
  */
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
