@@ -38,7 +38,7 @@ bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
 constexpr int64_t kComputeUnits = 256;    // MI355X; the default grid keeps every block resident
 constexpr int32_t kBlocksPerCu = 1;        // 4 waves per CU stream as fast as 8 and split the work less
-constexpr int64_t kMinTilesPerWave = 8;   // below this, fewer waves: merge cost beats parallelism
+constexpr int64_t kMinTilesPerWave = 4;   // below this, fewer waves: merge cost beats parallelism
 constexpr int64_t kMaxBlocks = 65535;
 constexpr int64_t kMaxTotalTiles = int64_t(1) << 40;
 

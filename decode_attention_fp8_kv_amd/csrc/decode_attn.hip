@@ -969,24 +969,32 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 }
 
 // ------------------------------------------------------------------------
-// The merge kernel: one wave per (sequence, KV head, query head of the
-// group), four per block.  Segments finished inside one wave were written
-// by the decode kernel; for the others, OR the partials' abort bits, then
-// combine the partials by log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M),
-// o = v_scale * sum acc_a 2^(m_a - M) / L, rounded to BF16.  Lanes hold
-// the statistics of 64 partials at a time and the output dims of the head;
-// each partial's accumulator row is one coalesced load per wave, and
-// kMergeUnroll of them are in flight at once.
+// The merge kernel: one item per (sequence, KV head, query head of the
+// group), handled by WPI waves (1 or 4; 4 / WPI items per block).  Segments
+// finished inside one wave were written by the decode kernel; for the
+// others, OR the partials' abort bits, then combine the partials by
+// log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M),
+// o = v_scale * sum acc_a 2^(m_a - M) / L, rounded to BF16.  The item's
+// waves split its partials; lanes hold the statistics of up to 64 partials
+// at a time and the head's output dims; each partial's accumulator row is
+// one coalesced load per wave, kMergeUnroll of them in flight per lane; with
+// WPI = 4 the waves' sums meet in LDS.  The host picks WPI = 4 when the grid
+// splits segments into many partials (small batches, long contexts).
 // ------------------------------------------------------------------------
 constexpr int kMergeUnroll = 16;
 
-template <int D>
+template <int D, int WPI>
 __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   constexpr int DL = D / 64;  // output dims per lane
-  const int lane = threadIdx.x & 63;
+  __shared__ float part_x[kWavesPerBlock][D];
+  __shared__ float part_l[kWavesPerBlock];
+  __shared__ float part_m[kWavesPerBlock];
+  __shared__ uint32_t part_bits[kWavesPerBlock];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = wave % WPI, w0 = wave - sub;  // this wave's share of the item; the item's first wave
   const int G = p.group;
-  const int64_t item = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  if (item >= (int64_t)p.batch * p.num_kv_heads * G) return;
+  const int64_t item = (int64_t)blockIdx.x * (kWavesPerBlock / WPI) + wave / WPI;
+  if (item >= (int64_t)p.batch * p.num_q_heads) return;  // uniform over the item's waves
   const int64_t seg = item / G;
   const int h = (int)(item - seg * G);
   const int b = (int)(seg / p.num_kv_heads), g = (int)(seg - (int64_t)b * p.num_kv_heads);
@@ -998,15 +1006,18 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   // a descriptor always names slots of this call's waves; never read past them
   if (2 * (first + n_arr) > 2 * (int64_t)p.num_blocks * kWavesPerBlock) return;
   auto slot_of = [&](int a) -> int64_t { return a == 0 ? first_slot : 2 * (first + a); };
+  // this wave's partials: [a_lo, a_hi)
+  const int a_lo = (int)((int64_t)n_arr * sub / WPI);
+  const int a_hi = (int)((int64_t)n_arr * (sub + 1) / WPI);
 
-  // abort bits and the maximum over all partials (lane a: partials a, a+64, ...)
+  // abort bits and the maximum (lane j: partials a_lo + j, + 64, ...)
   uint32_t bits = 0;
   float M = kNegInf, m0 = kNegInf, l0 = 0.f;
-  for (int a = lane; a < n_arr; a += 64) {
+  for (int a = a_lo + lane; a < a_hi; a += 64) {
     const int64_t sl = slot_of(a);
     bits |= p.part_status[sl];
     const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (sl * G + h) * 2);
-    if (a < 64) {
+    if (a < a_lo + 64) {
       m0 = ml[0];
       l0 = ml[1];
     }
@@ -1015,7 +1026,21 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   bits = (__any(bits & kAbortTag) ? kAbortTag : 0u) | (__any(bits & kAbortMeta) ? kAbortMeta : 0u);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = xor_max(M, off);
-  if (h == 0 && lane == 0) p.abort_flags[b] = (uint8_t)bits;
+  if constexpr (WPI > 1) {
+    if (lane == 0) {
+      part_bits[wave] = bits;
+      part_m[wave] = M;
+    }
+    __syncthreads();
+    bits = 0;
+    M = kNegInf;
+#pragma unroll
+    for (int i = 0; i < WPI; ++i) {
+      bits |= part_bits[w0 + i];
+      M = __builtin_fmaxf(M, part_m[w0 + i]);
+    }
+  }
+  if (h == 0 && sub == 0 && lane == 0) p.abort_flags[b] = (uint8_t)bits;
   if (bits != 0) return;
 
   // 64 partials at a time: lane j's weight 2^(m - M) is read by every lane
@@ -1024,16 +1049,16 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int k = 0; k < DL; ++k) x[k] = 0.f;
   const float* acc_h = p.part_acc + (int64_t)h * D + lane * DL;
-  for (int a0 = 0; a0 < n_arr; a0 += 64) {
+  for (int a0 = a_lo; a0 < a_hi; a0 += 64) {
     float m = m0, l = l0;
-    if (a0 > 0 && a0 + lane < n_arr) {
+    if (a0 > a_lo && a0 + lane < a_hi) {
       const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (slot_of(a0 + lane) * G + h) * 2);
       m = ml[0];
       l = ml[1];
     }
-    const float wgt = (a0 + lane < n_arr) ? fast_exp2(m - M) : 0.f;
+    const float wgt = (a0 + lane < a_hi) ? fast_exp2(m - M) : 0.f;
     Ls += l * wgt;
-    const int na = min(64, n_arr - a0);
+    const int na = min(64, a_hi - a0);
     for (int j0 = 0; j0 < na; j0 += kMergeUnroll) {
       float v[kMergeUnroll][DL];
 #pragma unroll
@@ -1061,12 +1086,31 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   }
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) Ls = xor_sum(Ls, off);
+  if constexpr (WPI > 1) {
+#pragma unroll
+    for (int k = 0; k < DL; ++k) part_x[wave][lane * DL + k] = x[k];
+    if (lane == 0) part_l[wave] = Ls;
+    __syncthreads();
+    if (sub != 0) return;
+    Ls = 0.f;
+#pragma unroll
+    for (int k = 0; k < DL; ++k) x[k] = 0.f;
+#pragma unroll
+    for (int i = 0; i < WPI; ++i) {
+      Ls += part_l[w0 + i];
+#pragma unroll
+      for (int k = 0; k < DL; ++k) x[k] += part_x[w0 + i][lane * DL + k];
+    }
+  }
   const float inv = p.v_scale / Ls;
+  float o[DL];
+#pragma unroll
+  for (int k = 0; k < DL; ++k) o[k] = x[k] * inv;
   uint16_t* out = p.out + ((int64_t)b * p.num_q_heads + (int64_t)g * G + h) * D + lane * DL;
   if constexpr (DL == 2) {
-    *reinterpret_cast<uint32_t*>(out) = f32_to_bf16_bits(x[0] * inv) | (f32_to_bf16_bits(x[1] * inv) << 16);
+    *reinterpret_cast<uint32_t*>(out) = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
   } else {
-    *out = (uint16_t)f32_to_bf16_bits(x[0] * inv);
+    *out = (uint16_t)f32_to_bf16_bits(o[0]);
   }
 }
 
@@ -1075,9 +1119,16 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), dim3(p.num_blocks), dim3(kBlockThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t merge_waves = (int64_t)p.batch * p.num_kv_heads * p.group;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)((merge_waves + kWavesPerBlock - 1) / kWavesPerBlock)),
-                     dim3(kBlockThreads), 0, stream, p);
+  const int64_t merge_items = (int64_t)p.batch * p.num_q_heads;  // one per query head
+  // Segments split into many partials (more waves than 16 per segment when
+  // every segment is as long as the page table allows) get 4 waves each.
+  const bool wide = (int64_t)p.num_blocks * kWavesPerBlock > 16 * (int64_t)p.batch * p.num_kv_heads;
+  if (wide) {
+    hipLaunchKernelGGL((merge_kernel<D, 4>), dim3((unsigned)merge_items), dim3(kBlockThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<D, 1>), dim3((unsigned)((merge_items + kWavesPerBlock - 1) / kWavesPerBlock)),
+                       dim3(kBlockThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
