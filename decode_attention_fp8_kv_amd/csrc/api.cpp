@@ -63,14 +63,14 @@ int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int3
 }
 
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t num_blocks) {
+                                 int32_t max_pages, int32_t num_blocks) {
   const size_t group = (size_t)(num_q_heads / num_kv_heads);
   const size_t segs = (size_t)batch * num_kv_heads;
   const size_t slots = 2 * (size_t)num_blocks * kWavesPerBlock;  // two partial slots per wave
   WorkspaceLayout w;
-  w.seg_desc = 0;
-  w.part_status = round_up(segs * sizeof(uint64_t), 256);
-  w.part_ml = w.part_status + round_up(slots * sizeof(uint32_t), 256);
+  w.check_bits = 0;
+  w.seg_desc = round_up((size_t)batch * check_chunks(max_pages), 256);
+  w.part_ml = w.seg_desc + round_up(segs * sizeof(uint64_t), 256);
   w.part_acc = w.part_ml + round_up(slots * group * 2 * sizeof(float), 256);
   w.total = w.part_acc + round_up(slots * group * head_dim * sizeof(float), 256);
   return w;
@@ -143,7 +143,7 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int3
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_blocks < 0) return 0;
   if (num_q_heads % num_kv_heads != 0 || !supported_head_dim(head_dim) || log2_page_size(page_size) < 0) return 0;
   const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kBlocksPerCu);
-  return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb).total;
+  return workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_pages, nb).total;
 }
 
 int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads) {
@@ -183,7 +183,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
   // resident blocks per CU: the FP8 MFMA kernel runs 2 waves per SIMD, the others 1
   const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kBlocksPerCu);
-  const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, nb);
+  const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_pages, nb);
   if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;
 
   const double log2e = 1.4426950408889634;
@@ -198,8 +198,9 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   p.out = out;
   p.abort_flags = abort_flags;
   uint8_t* base = static_cast<uint8_t*>(workspace);
+  p.check_bits = base + ws.check_bits;
+  p.check_chunks = check_chunks(max_pages);
   p.seg_desc = reinterpret_cast<uint64_t*>(base + ws.seg_desc);
-  p.part_status = reinterpret_cast<uint32_t*>(base + ws.part_status);
   p.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
   p.part_acc = reinterpret_cast<float*>(base + ws.part_acc);
   p.batch = batch;

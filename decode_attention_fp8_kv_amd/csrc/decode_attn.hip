@@ -15,19 +15,30 @@
 // over the L = seq_lens[b] tokens of KV head h / G, read through the page
 // table; nothing is written for a sequence whose pages fail the check.
 //
+// Kernels of one call
+// -------------------
+// 1. check_kernel (one block per 1024 page-table slots of a sequence)
+//    checks every page slot of every sequence -- page id in range, tag equal
+//    to the expected tag -- and the length.
+// 2. decode_kernel writes the abort flags and streams K/V for the
+//    sequences that passed.
+// 3. merge_kernel combines the partial results of split segments.
+// The check comes first so that an aborted sequence costs 12 bytes per page
+// (id, tag, expected tag) instead of its K/V, and is left out of the work
+// partition, which keeps the shares of the other sequences balanced.
+//
 // Work decomposition
 // ------------------
 // The batch's work is the flattened list of (sequence, KV head, 64-token
-// tile) triples.  A 1-D grid of blocks of 4 independent waves cuts it into
+// tile) triples of the sequences that passed the check.  A 1-D grid of blocks of 4 independent waves cuts it into
 // equal contiguous shares, one per wave (see "The balanced schedule"), so
 // every wave streams the same number of bytes whatever the length mix and
 // long sequences are split across waves (flash-decoding).  A wave keeps an
 // online-softmax state (running max m, sum l, unnormalized acc) per piece
 // of one (sequence, KV head); a piece that is a whole segment is finished in
 // registers, a partial piece is published to the workspace and the merge
-// kernel (one block per (sequence, KV head)) combines its partials
-// (log-sum-exp) in a second kernel and writes the output and the abort
-// flag.  No wave ever waits for another.
+// kernel combines the partials (log-sum-exp) and writes the output.  No
+// wave ever waits for another.
 
 // Per wave and tile (MFMA family, group of 5..16 query heads per KV head):
 //   * K rows: lane l loads a quarter of one token's row (bytes of dims
@@ -563,9 +574,8 @@ __device__ __forceinline__ void compute_tile(typename WaveState<KV, D, GM, MFMA>
 }
 
 template <int KV, int D, int GM, bool MFMA>
-__device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g, int L, int first_tile,
-                                             int n_wave_tiles, typename WaveState<KV, D, GM, MFMA>::T& st,
-                                             int lane, uint8_t* vstage) {
+__device__ __forceinline__ void run_wave(const DecodeParams& p, int b, int g, int L, int first_tile, int n_wave_tiles,
+                                         typename WaveState<KV, D, GM, MFMA>::T& st, int lane, uint8_t* vstage) {
   constexpr bool kVlds = MFMA && KV == 0;  // FP8 V streams through LDS
   using Tile = typename WaveState<KV, D, GM, MFMA>::Tile;
   const int log2ps = p.log2_page_size;
@@ -573,9 +583,8 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
   const int round_tiles = 64 >> ppt_log2;
   const int n_pages_b = (L + (1 << log2ps) - 1) >> log2ps;
   const int64_t pt_row = (int64_t)b * p.max_pages;
-  const bool tags_on = p.page_tags != nullptr;
-  uint32_t status = 0;
 
+  // The sequence passed the page check, so every page id read here is in range.
   for (int r0 = 0; r0 < n_wave_tiles; r0 += round_tiles) {
     const int rt = min(round_tiles, n_wave_tiles - r0);
     // lane j -> wave page j of this round
@@ -583,37 +592,20 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
     const int tile_j = first_tile + (r0 + jt);
     const int lp = log2ps < 6 ? (tile_j << ppt_log2) + (lane & ((1 << ppt_log2) - 1)) : (tile_j << 6) >> log2ps;
     const bool used = jt < rt && lp < n_pages_b;
-    int pid = used ? p.page_table[pt_row + lp] : 0;
-    const bool bad = used && (pid < 0 || pid >= p.num_pages);
-    uint32_t expected = 0;
-    if (tags_on && used) expected = p.expected_tags[pt_row + lp];
-    uint32_t actual = expected;
-    if (tags_on && used && !bad) actual = p.page_tags[pid];
-    const bool any_bad = __any(bad);
-
+    const int pid = used ? p.page_table[pt_row + lp] : 0;
     PageRound pr;
     pr.log2ps = log2ps;
     pr.ppt_log2 = ppt_log2;
     // Slots past the sequence's last page (only in its last tile) borrow the
     // tile's first page, which always exists; their rows are masked.
     const int first_pid = __shfl(pid, lane & ~((1 << ppt_log2) - 1));
-    pr.pid = (used && !bad) ? pid : first_pid;
+    pr.pid = used ? pid : first_pid;
 
-    const bool go = status == 0 && !any_bad;
     Tile ta, tb;
     const uint8_t *kp, *vp;
-    if (go) {
-      // Speculative: page ids are range-checked; data is not used before the tag ballot.
-      tile_pointers<KV, D, GM, MFMA>(p, pr, 0, first_tile + r0, g, lane, kp, vp);
-      load_tile<KV, D, GM, MFMA>(ta, kp, vp);
-      if constexpr (kVlds) v_tile_to_lds<D>(p, pr, 0, first_tile + r0, g, lane, vstage);
-    }
-    const bool any_mismatch = __any(actual != expected);
-    status |= (any_bad ? kAbortMeta : 0u) | (any_mismatch ? kAbortTag : 0u);
-    if (status != 0) {
-      if constexpr (kVlds) __builtin_amdgcn_s_waitcnt(0);  // no copy may still be landing in LDS
-      continue;  // keep checking later rounds; compute nothing
-    }
+    tile_pointers<KV, D, GM, MFMA>(p, pr, 0, first_tile + r0, g, lane, kp, vp);
+    load_tile<KV, D, GM, MFMA>(ta, kp, vp);
+    if constexpr (kVlds) v_tile_to_lds<D>(p, pr, 0, first_tile + r0, g, lane, vstage);
 
     if constexpr (kVlds) {
       // Per tile i: V(i) out of LDS; start V(i+1) into LDS; QK(i) from the K
@@ -659,7 +651,6 @@ __device__ __forceinline__ uint32_t run_wave(const DecodeParams& p, int b, int g
     }
     }
   }
-  return status;
 }
 
 // ------------------------------------------------------------------------
@@ -811,8 +802,9 @@ __device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t
 // the wave whose range holds flattened index x
 __device__ __forceinline__ int64_t wave_of(int64_t x, int64_t total, int64_t nw) { return ((x + 1) * nw - 1) / total; }
 
-__device__ __forceinline__ int seq_tiles(int L, int max_tokens) {
-  return (L >= 1 && L <= max_tokens) ? (L + kTileTokens - 1) / kTileTokens : 0;
+// tiles of sequence b's segments, 0 if it failed the page check
+__device__ __forceinline__ int seq_tiles(int L, int max_tokens, uint32_t abort_bits) {
+  return (abort_bits == 0 && L >= 1 && L <= max_tokens) ? (L + kTileTokens - 1) / kTileTokens : 0;
 }
 
 __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
@@ -880,17 +872,12 @@ __device__ __forceinline__ void wave_piece(const DecodeParams& p, uint8_t* vstag
     }
   }
 
-  const uint32_t status = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo, t_hi - t_lo, st, lane, vstage);
-  const int64_t out_row0 = ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
-
+  run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo, t_hi - t_lo, st, lane, vstage);
   const int64_t seg = (int64_t)b * p.num_kv_heads + g;
   if (t_lo == 0 && t_hi == T) {
     // The whole segment is here: finish it.
-    if (lane == 0) {
-      p.abort_flags[b] = (uint8_t)status;
-      p.seg_desc[seg] = 0;
-    }
-    if (status == 0) wave_output(st, p, out_row0, lane);
+    if (lane == 0) p.seg_desc[seg] = 0;
+    wave_output(st, p, ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D, lane);
     return;
   }
   if (t_lo == 0 && lane == 0) {
@@ -900,11 +887,66 @@ __device__ __forceinline__ void wave_piece(const DecodeParams& p, uint8_t* vstag
     const uint32_t n_part = (uint32_t)(wave_of(seg_lo + T - 1, TT, nw) - w + 1);
     p.seg_desc[seg] = first_slot | ((uint64_t)n_part << 32);
   }
-
   // A partial piece: publish it; the merge kernel combines the partials.
-  const int64_t slot = 2 * w + ((seg_lo + t_lo) == r0 ? 0 : 1);
-  if (status == 0) wave_publish(st, p, slot, lane);
-  if (lane == 0) p.part_status[slot] = status;
+  wave_publish(st, p, 2 * w + ((seg_lo + t_lo) == r0 ? 0 : 1), lane);
+}
+
+// ------------------------------------------------------------------------
+// The page check, before any K/V is read: one block per (1024-slot chunk of
+// the page table, sequence).  Every page slot j < ceil(L / page_size) of
+// sequence b is checked: the id must lie in [0, num_pages) (else bit
+// kAbortMeta) and, when tags are on, the page's current tag must equal the
+// tag the sequence recorded for that slot (else bit kAbortTag); a length
+// outside [1, max_pages * page_size] is kAbortMeta.  Each block writes its
+// chunk's bits; the decode kernel ORs a sequence's chunks into its abort
+// flag.  Page ids and expected tags are loaded for the whole chunk of the
+// table row (always in bounds) while the length is still in flight, so the
+// check costs two dependent loads.
+// ------------------------------------------------------------------------
+constexpr int kCheckUnroll = 4;                             // slots per thread
+constexpr int kCheckChunk = kCheckUnroll * kBlockThreads;   // slots per block
+static_assert(kCheckChunk == kCheckSlots, "the host sizes the check grid with kCheckSlots");
+
+__global__ __launch_bounds__(kBlockThreads) void check_kernel(DecodeParams p) {
+  const int c = blockIdx.x, b = blockIdx.y;
+  const int L = p.seq_lens[b];
+  const int64_t row = (int64_t)b * p.max_pages;
+  const bool tags_on = p.page_tags != nullptr;
+  int pid[kCheckUnroll];
+  uint32_t expected[kCheckUnroll];
+#pragma unroll
+  for (int u = 0; u < kCheckUnroll; ++u) {
+    const int j = c * kCheckChunk + u * kBlockThreads + threadIdx.x;
+    pid[u] = j < p.max_pages ? p.page_table[row + j] : 0;
+    expected[u] = (tags_on && j < p.max_pages) ? p.expected_tags[row + j] : 0u;
+  }
+  const int max_tokens = p.max_pages << p.log2_page_size;
+  uint32_t bits = 0;
+  if (L < 1 || L > max_tokens) {
+    bits = kAbortMeta;
+  } else {
+    const int n_pages = (L + (1 << p.log2_page_size) - 1) >> p.log2_page_size;
+#pragma unroll
+    for (int u = 0; u < kCheckUnroll; ++u) {
+      const int j = c * kCheckChunk + u * kBlockThreads + threadIdx.x;
+      if (j >= n_pages) continue;
+      if (pid[u] < 0 || pid[u] >= p.num_pages)
+        bits |= kAbortMeta;
+      else if (tags_on && p.page_tags[pid[u]] != expected[u])
+        bits |= kAbortTag;
+    }
+  }
+  const int any_tag = __syncthreads_or((int)(bits & kAbortTag));
+  const int any_meta = __syncthreads_or((int)(bits & kAbortMeta));
+  if (threadIdx.x == 0)
+    p.check_bits[(int64_t)b * p.check_chunks + c] = (uint8_t)((any_tag ? kAbortTag : 0u) | (any_meta ? kAbortMeta : 0u));
+}
+
+// Abort bits of sequence b: the OR of its chunks' check results.
+__device__ __forceinline__ uint32_t seq_abort_bits(const DecodeParams& p, int b) {
+  uint32_t bits = 0;
+  for (int c = 0; c < p.check_chunks; ++c) bits |= p.check_bits[(int64_t)b * p.check_chunks + c];
+  return bits;
 }
 
 // ------------------------------------------------------------------------
@@ -921,14 +963,18 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
   const int max_tokens = p.max_pages << p.log2_page_size;
   const int64_t hkv = p.num_kv_heads;
 
-  // ---- pass 1: total work; wave 0 flags sequences with unusable lengths
+  // ---- pass 1: total work of the sequences that passed the page check;
+  // wave 0 writes every abort flag and marks the failed sequences' segments
+  // as having nothing to merge
   int64_t mine = 0;
   for (int b = lane; b < p.batch; b += 64) {
-    const int T = seq_tiles(p.seq_lens[b], max_tokens);
+    const uint32_t bits = seq_abort_bits(p, b);
+    const int T = seq_tiles(p.seq_lens[b], max_tokens, bits);
     mine += T;
-    if (T == 0 && w == 0) {
-      p.abort_flags[b] = (uint8_t)kAbortMeta;
-      for (int g = 0; g < p.num_kv_heads; ++g) p.seg_desc[(int64_t)b * p.num_kv_heads + g] = 0;
+    if (w == 0) {
+      p.abort_flags[b] = (uint8_t)bits;
+      if (T == 0)
+        for (int g = 0; g < p.num_kv_heads; ++g) p.seg_desc[(int64_t)b * p.num_kv_heads + g] = 0;
     }
   }
   const int64_t TT = wave_sum64(mine) * hkv;
@@ -943,7 +989,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
   for (int c = 0; c < p.batch; c += 64) {
     if (carry * hkv >= r1) break;
     const int b = c + lane;
-    const int T = b < p.batch ? seq_tiles(p.seq_lens[b], max_tokens) : 0;
+    const int T = b < p.batch ? seq_tiles(p.seq_lens[b], max_tokens, seq_abort_bits(p, b)) : 0;
     const int64_t incl = wave_inclusive_scan64(T, lane);
     const int64_t excl = carry + incl - T;
     const bool hit = T > 0 && excl * hkv < r1 && (excl + T) * hkv > r0;
@@ -971,8 +1017,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 // ------------------------------------------------------------------------
 // The merge kernel: one item per (sequence, KV head, query head of the
 // group), handled by WPI waves (1 or 4; 4 / WPI items per block).  Segments
-// finished inside one wave were written by the decode kernel; for the
-// others, OR the partials' abort bits, then combine the partials by
+// finished inside one wave were written by the decode kernel, and aborted
+// sequences have no descriptor; the others' partials are combined by
 // log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M),
 // o = v_scale * sum acc_a 2^(m_a - M) / L, rounded to BF16.  The item's
 // waves split its partials; lanes hold the statistics of up to 64 partials
@@ -989,7 +1035,6 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   __shared__ float part_x[kWavesPerBlock][D];
   __shared__ float part_l[kWavesPerBlock];
   __shared__ float part_m[kWavesPerBlock];
-  __shared__ uint32_t part_bits[kWavesPerBlock];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = wave % WPI, w0 = wave - sub;  // this wave's share of the item; the item's first wave
   const int G = p.group;
@@ -1000,7 +1045,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   const int b = (int)(seg / p.num_kv_heads), g = (int)(seg - (int64_t)b * p.num_kv_heads);
   const uint64_t desc = p.seg_desc[seg];
   const int n_arr = (int)(desc >> 32);
-  if (n_arr < 2) return;  // finished inside one wave, or an unusable length
+  if (n_arr < 2) return;  // finished inside one wave, or aborted
   const int64_t first_slot = (uint32_t)desc;
   const int64_t first = first_slot >> 1;
   // a descriptor always names slots of this call's waves; never read past them
@@ -1010,38 +1055,25 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
   const int a_lo = (int)((int64_t)n_arr * sub / WPI);
   const int a_hi = (int)((int64_t)n_arr * (sub + 1) / WPI);
 
-  // abort bits and the maximum (lane j: partials a_lo + j, + 64, ...)
-  uint32_t bits = 0;
+  // the maximum (lane j: partials a_lo + j, + 64, ...)
   float M = kNegInf, m0 = kNegInf, l0 = 0.f;
   for (int a = a_lo + lane; a < a_hi; a += 64) {
-    const int64_t sl = slot_of(a);
-    bits |= p.part_status[sl];
-    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (sl * G + h) * 2);
+    const f32x2_t ml = *reinterpret_cast<const f32x2_t*>(p.part_ml + (slot_of(a) * G + h) * 2);
     if (a < a_lo + 64) {
       m0 = ml[0];
       l0 = ml[1];
     }
     M = __builtin_fmaxf(M, ml[0]);
   }
-  bits = (__any(bits & kAbortTag) ? kAbortTag : 0u) | (__any(bits & kAbortMeta) ? kAbortMeta : 0u);
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) M = xor_max(M, off);
   if constexpr (WPI > 1) {
-    if (lane == 0) {
-      part_bits[wave] = bits;
-      part_m[wave] = M;
-    }
+    if (lane == 0) part_m[wave] = M;
     __syncthreads();
-    bits = 0;
     M = kNegInf;
 #pragma unroll
-    for (int i = 0; i < WPI; ++i) {
-      bits |= part_bits[w0 + i];
-      M = __builtin_fmaxf(M, part_m[w0 + i]);
-    }
+    for (int i = 0; i < WPI; ++i) M = __builtin_fmaxf(M, part_m[w0 + i]);
   }
-  if (h == 0 && sub == 0 && lane == 0) p.abort_flags[b] = (uint8_t)bits;
-  if (bits != 0) return;
 
   // 64 partials at a time: lane j's weight 2^(m - M) is read by every lane
   float Ls = 0.f;
@@ -1116,6 +1148,9 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
 
 template <int KV, int D, int GM, bool MFMA>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(check_kernel, dim3(p.check_chunks, p.batch), dim3(kBlockThreads), 0, stream, p);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
   hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), dim3(p.num_blocks), dim3(kBlockThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -35,13 +35,14 @@ struct DecodeParams {
   const uint32_t* expected_tags;    // [B][max_pages] or null
   uint16_t* out;                    // bf16 [B][Hq][D]
   uint8_t* abort_flags;             // [B]
+  uint8_t* check_bits;              // [B][check_chunks] abort bits found by the page check
   uint64_t* seg_desc;               // [B*Hkv] first partial slot | number of partials << 32 (< 2: none)
-  uint32_t* part_status;            // [2*waves]        abort bits of each partial piece
   float* part_ml;                   // [2*waves][G][2]  running max (log2 domain), sum
   float* part_acc;                  // [2*waves][G][D]  unnormalized output
   int32_t batch, num_q_heads, num_kv_heads, group, max_pages, num_pages;
   int32_t log2_page_size;
   int32_t num_blocks;               // grid size; each of its 4*num_blocks waves owns an equal share
+  int32_t check_chunks;             // page-check blocks per sequence (1024 page slots each)
   float qk_scale_log2;              // softmax_scale * k_scale * log2(e)
   float v_scale;                    // folded into the final normalization
 };
@@ -51,10 +52,12 @@ int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int3
                     int32_t num_blocks, int32_t blocks_per_cu);
 
 struct WorkspaceLayout {
-  size_t seg_desc, part_status, part_ml, part_acc, total;
+  size_t check_bits, seg_desc, part_ml, part_acc, total;
 };
 WorkspaceLayout workspace_layout(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t num_blocks);
+                                 int32_t head_dim, int32_t max_pages, int32_t num_blocks);
+constexpr int32_t kCheckSlots = 1024;  // page-table slots per page-check block
+inline int32_t check_chunks(int32_t max_pages) { return (max_pages + kCheckSlots - 1) / kCheckSlots; }
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,

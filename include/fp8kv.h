@@ -177,8 +177,11 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *                  floating-point rounding, and repeated calls with the same
  *                  inputs and n give bit-identical outputs.
  *
- * A call enqueues two kernels on the stream: the decode kernel and a merge
- * kernel that combines the partial results of segments split between waves.
+ * A call enqueues three kernels on the stream: a page check (one block per
+ * sequence; writes abort_flags), the decode kernel (which reads K/V only of
+ * the sequences that passed, so an aborted sequence costs 12 bytes per
+ * page), and a merge kernel that combines the partial results of segments
+ * split between waves.
  *
  * Tag rule: for every page slot j < ceil(L / page_size) (the partial last
  * page included), the page id p = page_table[b*max_pages + j] must lie in
