@@ -84,8 +84,22 @@ class Case:
         self.flags = torch.empty(w.batch, dtype=torch.uint8, device=dev)
         self.ws = fk.alloc_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
                                      w.max_pages, device=dev)
-        fk.kv_quant_append(w.ctx_k, w.ctx_v, w.ctx_seq, w.ctx_pos, self.pt, w.k_scale, w.v_scale,
-                           self.kc, self.vc, kv_dtype)
+        # Bulk fill of the cache (every context row), timed on its second run
+        # (the first one also loads the kernel's code object).
+        fill_ms = []
+        for _ in range(2):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fk.kv_quant_append(w.ctx_k, w.ctx_v, w.ctx_seq, w.ctx_pos, self.pt, w.k_scale, w.v_scale,
+                               self.kc, self.vc, kv_dtype)
+            b.record()
+            torch.cuda.synchronize(dev)
+            fill_ms.append(a.elapsed_time(b))
+        n_el = 2 * w.ctx_k.numel()                   # K and V elements
+        per_el = 3 if kv_dtype == fk.KV_FP8_E4M3 else 4  # bf16 read + cache element written
+        self.fill = {"rows": int(w.ctx_k.shape[0]), "us": round(fill_ms[-1] * 1e3, 1),
+                     "gbps": round(n_el * per_el / (fill_ms[-1] * 1e-3) / 1e9, 1),
+                     "bytes_per_element": per_el}
         self.new = (w.new_k.contiguous(), w.new_v.contiguous(), w.new_seq, w.new_pos)
         torch.cuda.synchronize(dev)
 
@@ -108,22 +122,48 @@ class Case:
 
 def time_steps(case, steps, warmup):
     """Warm up, then time exactly `steps` steps between two synchronizations;
-    HIP events on the launch stream bracket each decode launch."""
+    HIP events on the launch stream bracket each append and each decode call."""
     torch = case.torch
     for _ in range(warmup):
         case.step()
     torch.cuda.synchronize(case.dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     t0 = time.perf_counter()
     for i in range(steps):
-        case.append()
         ev[i][0].record()
-        case.decode(tags=True)
+        case.append()
         ev[i][1].record()
+        case.decode(tags=True)
+        ev[i][2].record()
     torch.cuda.synchronize(case.dev)
     wall = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    return wall, dec_ms
+    app_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    dec_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    return wall, dec_ms, app_ms
+
+
+def time_flushed(case, iters=30, flush_bytes=1 << 30):
+    """Per-call protocol: before each timed call, outside the timed region, a
+    1 GiB read evicts the 256 MB Infinity Cache and the L2s (a read, not a
+    write: a 1 GiB write would leave up to 256 MB of dirty lines that the
+    timed call then pays to write back); HIP events bracket the single call.
+    Returns (median, p95) in microseconds."""
+    torch = case.torch
+    scratch = torch.ones(flush_bytes, dtype=torch.uint8, device=case.dev)
+    sink = torch.empty(1, dtype=torch.uint8, device=case.dev)
+    for _ in range(5):
+        case.decode(True)
+    ms = []
+    for _ in range(iters):
+        sink[0] = scratch.max()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        case.decode(True)
+        b.record()
+        torch.cuda.synchronize(case.dev)
+        ms.append(a.elapsed_time(b))
+    del scratch, sink
+    return round(float(np.median(ms)) * 1e3, 2), round(float(np.percentile(ms, 95)) * 1e3, 2)
 
 
 def tag_overhead(case, iters=100):
@@ -211,11 +251,22 @@ def cpu_baseline(w, budget_s=15.0):
         if elapsed >= budget_s:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(len(done) / elapsed, 3),
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu_model": cpu_model,
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "sample": f"{len(done)} of {w.batch} sequences ({tokens} cached tokens), one decode step each, "
                   f"{elapsed:.1f} s of CPU time; numpy fp64 with {threads} BLAS threads",
     }
@@ -347,7 +398,7 @@ def main():
             continue
         case = Case(w, kv, dev)
         torch.cuda.synchronize(dev)
-        wall, dec_ms = time_steps(case, args.steps, args.warmup)
+        wall, dec_ms, app_ms = time_steps(case, args.steps, args.warmup)
         flags = case.flags.cpu().numpy()
         alg = algorithmic_bytes(w, kv, flags)
         ok = int((flags == 0).sum())
@@ -361,6 +412,9 @@ def main():
             "alg_bytes": alg,
             "gbps": alg / (mean_us * 1e-6) / 1e9,
             "aborted": int(w.batch - ok),
+            "append_median_us": float(np.median(app_ms)) * 1e3,
+            "fill": case.fill,
+            "flushed": time_flushed(case),
         }
         if name == "fp8":
             res["tags"] = tag_overhead(case)
@@ -412,6 +466,11 @@ def main():
             "traffic": traffic,
         },
         "tag_check": res.get("tags"),
+        "decode_us_flushed": {"median": f["flushed"][0], "p95": f["flushed"][1],
+                              "protocol": "1 GiB read before each call (evicts the Infinity Cache), "
+                                          "outside the timed region; 30 calls"},
+        "append_32_rows_us": round(f["append_median_us"], 2),
+        "bulk_fill": f["fill"],
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }
     if "bf16" in res:

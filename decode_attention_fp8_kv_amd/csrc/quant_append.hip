@@ -7,24 +7,42 @@
 // Each element x becomes e4m3(fp32(x) / scale): an IEEE fp32 division, then
 // round-to-nearest-even with saturation at +-448.
 //
-// One thread moves 8 consecutive elements of one (row, KV head) for both K
-// and V: a 16-byte BF16 load each, 8-byte (FP8) or 16-byte (BF16) stores.
-// Consecutive threads cover consecutive elements of a row, so loads and
-// stores are fully coalesced; a row of one head is one contiguous run of
-// head_dim elements in its page.
+// One thread moves 16 consecutive elements of one (row, KV head) for both K
+// and V: two 16-byte BF16 loads each, one 16-byte (FP8) or two (BF16)
+// stores.  Consecutive threads cover consecutive elements of a row, so loads
+// and stores are fully coalesced; a row of one head is one contiguous run
+// of head_dim elements in its page.  Sixteen independent divisions per
+// tensor and thread keep the IEEE division's dependency chains overlapped.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace fp8kv {
 namespace {
 
+constexpr int kChunk = 16;  // elements per thread
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
+
+// 16 BF16 elements (two 16-byte words) -> 16 e4m3 codes of fp32(x) / s.
+__device__ __forceinline__ u32x4_t quant16(const u32x4_t (&in)[2], float s) {
+  u32x4_t out;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {  // output word q = elements 4q .. 4q+3
+    const uint32_t w0 = in[q >> 1][2 * (q & 1)], w1 = in[q >> 1][2 * (q & 1) + 1];
+    out[q] = e4m3_encode_pair(bf16_lo(w0) / s, bf16_hi(w0) / s) |
+             (e4m3_encode_pair(bf16_lo(w1) / s, bf16_hi(w1) / s) << 16);
+  }
+  return out;
+}
+
 template <int KV>
 __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
-  const int chunks_per_row = (p.num_kv_heads * p.head_dim) >> 3;
+  const int chunks_per_row = (p.num_kv_heads * p.head_dim) / kChunk;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)p.n_rows * chunks_per_row) return;
   const int row = (int)(idx / chunks_per_row);
-  const int e0 = (int)(idx - (int64_t)row * chunks_per_row) << 3;  // element within the row
+  const int e0 = (int)(idx - (int64_t)row * chunks_per_row) * kChunk;  // element within the row
   const int head = e0 / p.head_dim;
   const int d0 = e0 - head * p.head_dim;
 
@@ -38,39 +56,28 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
   const int64_t dst = (((int64_t)page * p.num_kv_heads + head) * page_size + slot) * p.head_dim + d0;
   const int64_t src = (int64_t)row * p.num_kv_heads * p.head_dim + e0;
 
-  const u32x4_t kin = *reinterpret_cast<const u32x4_t*>(p.k_new + src);
-  const u32x4_t vin = *reinterpret_cast<const u32x4_t*>(p.v_new + src);
+  u32x4_t kin[2], vin[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    kin[h] = *reinterpret_cast<const u32x4_t*>(p.k_new + src + 8 * h);
+    vin[h] = *reinterpret_cast<const u32x4_t*>(p.v_new + src + 8 * h);
+  }
   if constexpr (KV == 0) {
-    u32x2_t kout, vout;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t kb[2], vb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t kw = kin[2 * half + j], vw = vin[2 * half + j];
-        // element 2j+0 is the low half-word, 2j+1 the high one
-        const float k0 = __builtin_bit_cast(float, kw << 16) / p.k_scale;
-        const float k1 = __builtin_bit_cast(float, kw & 0xFFFF0000u) / p.k_scale;
-        const float v0 = __builtin_bit_cast(float, vw << 16) / p.v_scale;
-        const float v1 = __builtin_bit_cast(float, vw & 0xFFFF0000u) / p.v_scale;
-        kb[j] = e4m3_encode_pair(k0, k1);
-        vb[j] = e4m3_encode_pair(v0, v1);
-      }
-      kout[half] = kb[0] | (kb[1] << 16);
-      vout[half] = vb[0] | (vb[1] << 16);
-    }
-    *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = kout;
-    *reinterpret_cast<u32x2_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = vout;
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = quant16(kin, p.k_scale);
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = quant16(vin, p.v_scale);
   } else {
-    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.k_cache) + dst) = kin;
-    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.v_cache) + dst) = vin;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.k_cache) + dst + 8 * h) = kin[h];
+      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.v_cache) + dst + 8 * h) = vin[h];
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.n_rows * ((p.num_kv_heads * p.head_dim) >> 3);
+  const int64_t threads = (int64_t)p.n_rows * ((p.num_kv_heads * p.head_dim) / kChunk);
   if (threads == 0) return hipSuccess;
   const int64_t blocks = (threads + 255) / 256;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;

@@ -61,6 +61,44 @@ def test_append_fp8_all_bf16_patterns(gpu_device, scale, hkv, d, ps):
     assert np.array_equal(gv, ovc)
 
 
+def _many_scales():
+    """Scales that stress the multiply-and-correct quotient: subnormal and
+    near-overflow scales, scales whose reciprocal is inexact, and 16 seeded
+    log-uniform ones."""
+    fixed = [3 * 2.0 ** -149, 1e-40, 2.0 ** -126, 1e-30, 3.3e-9, 2.0 ** -10, 0.3, 1.0000001, 1.7, 3.0,
+             448.0, 1e10, 3.0e38]
+    rng = np.random.default_rng(11)
+    return fixed + [float(np.float32(2.0 ** e)) for e in rng.uniform(-120, 120, 16)]
+
+
+@pytest.mark.parametrize("scale", _many_scales())
+def test_append_fp8_all_bf16_patterns_many_scales(gpu_device, scale):
+    say(f"append fp8 all-bf16 scale={scale!r} (many scales)")
+    hkv, d, ps = 8, 128, 64
+    t, rows = _all_bf16_rows(hkv, d)
+    n = rows.shape[0]
+    pt, seq, pos, pool = _layout(n, ps, 2, seed=7)
+    shape = (pool, hkv, ps, d)
+    kc = torch.full(shape, 0xA5, dtype=torch.uint8, device=gpu_device)
+    vc = torch.full(shape, 0x5A, dtype=torch.uint8, device=gpu_device)
+    vt = torch.flip(t.view(-1), [0]).view(t.shape).contiguous()
+    v_scale = float(np.float32(scale * 1.37))
+    if not np.isfinite(v_scale) or v_scale <= 0:
+        v_scale = scale
+    fk.kv_quant_append(t.to(gpu_device), vt.to(gpu_device), torch.from_numpy(seq).to(gpu_device),
+                       torch.from_numpy(pos).to(gpu_device), torch.from_numpy(pt).to(gpu_device),
+                       scale, v_scale, kc, vc, fk.KV_FP8_E4M3)
+    torch.cuda.synchronize()
+    okc = np.full(shape, 0xA5, np.uint8)
+    ovc = np.full(shape, 0x5A, np.uint8)
+    pa.append(rows, W.bits_u16(vt), seq, pos, pt, scale, v_scale, okc, ovc, pa.KV_FP8_E4M3)
+    gk, gv = pool_bits(kc), pool_bits(vc)
+    bad = np.nonzero(gk.ravel() != okc.ravel())[0]
+    assert bad.size == 0, f"{bad.size} K bytes differ, first at {bad[:5]}"
+    badv = np.nonzero(gv.ravel() != ovc.ravel())[0]
+    assert badv.size == 0, f"{badv.size} V bytes differ, first at {badv[:5]}"
+
+
 def test_append_bf16_copies_bits(gpu_device):
     say("append bf16 copy all patterns")
     hkv, d, ps = 2, 64, 16
