@@ -304,20 +304,22 @@ def summarize_profiles(out_dir: str) -> None:
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     avg = {}
     for r in keep:
-        name = r["Name"].replace("void fp8kv::(anonymous namespace)::", "").replace("(fp8kv::DecodeParams)", "")
+        name = r["Name"].replace("void ", "").replace("fp8kv::(anonymous namespace)::", "")
+        name = name.replace("(fp8kv::DecodeParams)", "")
         name = name.replace("(fp8kv::AppendParams)", "")
         avg[name] = float(r["AverageNs"]) / 1e3
         lines.append(f"| `{name}` | {r['Calls']} | {avg[name]:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} |")
     dec = avg.get("decode_kernel<0, 128, 16, true>")
-    mrg = avg.get("merge_kernel<128>")
-    if dec is not None and mrg is not None:
-        lines += ["", f"One FP8 `paged_decode_attn` call = decode_kernel<0, 128, 16, true> + merge_kernel<128> = "
-                      f"{dec:.2f} + {mrg:.2f} = {dec + mrg:.2f} us of kernel time (the merge kernel's average "
-                      f"covers the FP8 and BF16 calls).",
+    mrg = next((v for k, v in avg.items() if k.startswith("merge_kernel<128")), None)
+    chk = next((v for k, v in avg.items() if k.startswith("check_kernel")), None)
+    if dec is not None and mrg is not None and chk is not None:
+        lines += ["", f"One FP8 `paged_decode_attn` call = check_kernel + decode_kernel<0, 128, 16, true> + "
+                      f"merge_kernel<128, 1> = {chk:.2f} + {dec:.2f} + {mrg:.2f} = {chk + dec + mrg:.2f} us of kernel "
+                      f"time (the check and merge averages cover the FP8 and BF16 calls).",
                   "decode_kernel<0,...> is the FP8-cache instance, decode_kernel<1,...> the BF16 one; "
-                  "quant_append_kernel<0>/<1> are kv_quant_append (their averages include the one-off fill of "
-                  "the whole cache before timing)."]
+                  "quant_append_kernel<0>/<1> are kv_quant_append (their averages mix the 32-row appends of the "
+                  "timed steps with the two bulk fills of the whole cache before timing)."]
     lines.append("")
     with open(PROFILE_TRACE, "w") as f:
         f.write("\n".join(lines))
@@ -332,16 +334,18 @@ def summarize_profiles(out_dir: str) -> None:
         big = [v for v in copy if v >= 0.9 * max(copy)]
         factor = COPY_BYTES / (sum(big) / len(big) * 1024.0)
         dk = [v for k, v in vals.items() if "decode_kernel<0, 128, 16, true>" in k for v in v]
-        mk = [v for k, v in vals.items() if "merge_kernel<128>" in k for v in v]
-        per[key] = (factor, sum(dk) / len(dk), sum(mk) / len(mk), len(dk), len(big))
-    ff, fd, fm, nd, nc = per["fetch"]
-    wf, wd, wm, _, _ = per["write"]
-    traffic = (fd + fm) * 1024.0 * ff + (wd + wm) * 1024.0 * wf
+        mk = [v for k, v in vals.items() if "merge_kernel<128" in k for v in v]
+        ck = [v for k, v in vals.items() if "check_kernel" in k for v in v]
+        per[key] = (factor, sum(dk) / len(dk), sum(mk) / len(mk), sum(ck) / len(ck), len(dk), len(big))
+    ff, fd, fm, fc, nd, nc = per["fetch"]
+    wf, wd, wm, wc, _, _ = per["write"]
+    traffic = (fd + fm + fc) * 1024.0 * ff + (wd + wm + wc) * 1024.0 * wf
     from decode_attention_fp8_kv_amd import workloads as W
     w = W.make(WORKLOAD)
     alg = algorithmic_bytes(w, 0)
     out = [
-        "# HBM traffic of one FP8 paged_decode_attn call (decode_kernel<0, 128, 16, true> + merge_kernel<128>)",
+        "# HBM traffic of one FP8 paged_decode_attn call (check_kernel + decode_kernel<0, 128, 16, true> +",
+        "# merge_kernel<128, 1>)",
         "# on the conc32 workload, from two rocprofv3 counter passes (from the repository root; OUT is any folder):",
         "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
         "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["write"],
@@ -352,8 +356,10 @@ def summarize_profiles(out_dir: str) -> None:
         f"copy_dispatches: {nc}",
         f"fetch_kib_per_dispatch_decode: {fd:.1f}",
         f"fetch_kib_per_dispatch_merge: {fm:.1f}",
+        f"fetch_kib_per_dispatch_check: {fc:.1f}",
         f"write_kib_per_dispatch_decode: {wd:.1f}",
         f"write_kib_per_dispatch_merge: {wm:.1f}",
+        f"write_kib_per_dispatch_check: {wc:.1f}",
         f"fetch_scale: {ff:.4f}",
         f"write_scale: {wf:.4f}",
         f"traffic_bytes_per_launch: {traffic:.0f}",
@@ -457,7 +463,7 @@ def main():
         "decode_us": {"mean": round(f["decode_mean_us"], 2), "median": round(f["decode_median_us"], 2),
                       "p95": round(f["decode_p95_us"], 2)},
         "roofline": {
-            "kernel": "paged_decode_attn FP8: decode_kernel<0,128,16,true> + merge_kernel<128>",
+            "kernel": "paged_decode_attn FP8: check_kernel + decode_kernel<0,128,16,true> + merge_kernel<128,1>",
             "bound": "hbm",
             "achieved": round(f["gbps"], 1),
             "peak": PEAK_HBM_GBPS,
