@@ -28,9 +28,11 @@ Specification (OFP8)", E4M3 encoding, cited as [OFP8].
 Modules:
 * ``oracle.e4m3``       -- e4m3 decode/encode and the two-rounding quantizer.
 * ``oracle.paged_attn`` -- append scatter, tag/abort rule, fp64 attention.
+* ``oracle.page_pool``  -- generation-tagged page allocator (alloc/free) and
+  the tag-checked append.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``; no
 function here is "parity unpinned".
 """
 
-from . import e4m3, paged_attn  # noqa: F401
+from . import e4m3, page_pool, paged_attn  # noqa: F401
