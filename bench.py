@@ -216,6 +216,64 @@ def copy_bandwidth(dev, nbytes=2 << 30, reps=10):
     return gbps
 
 
+def pool_timings(dev, batch=32, max_pages=513, reps=20):
+    """Median HIP-event time of the page-pool calls at the benchmark's shape:
+    a decode step's growth (one page for each of 32 sequences), a prefill's
+    (512 pages each), freeing all 32 sequences, and a 32-row checked append.
+    All are single small kernels, so they are reported in microseconds."""
+    import torch
+    import decode_attention_fp8_kv_amd as fk
+
+    num_pages = batch * max_pages
+    free_pages = torch.empty(num_pages, dtype=torch.int32, device=dev)
+    free_count = torch.empty(1, dtype=torch.int32, device=dev)
+    counts = torch.zeros(batch, dtype=torch.int32, device=dev)
+    table = torch.full((batch, max_pages), -1, dtype=torch.int32, device=dev)
+    expected = torch.zeros((batch, max_pages), dtype=torch.int32, device=dev)
+    tags = torch.zeros(num_pages, dtype=torch.int32, device=dev)
+    status = torch.empty(batch, dtype=torch.uint8, device=dev)
+    one = torch.ones(batch, dtype=torch.int32, device=dev)
+    prefill = torch.full((batch,), 512, dtype=torch.int32, device=dev)
+    release = torch.ones(batch, dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        ms = []
+        for _ in range(reps):
+            fk.page_pool_init(free_pages, free_count)
+            counts.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize(dev)
+            ms.append(a.elapsed_time(b))
+        return round(float(np.median(ms)) * 1e3, 2)
+
+    res = {
+        "alloc_32x1_us": timed(lambda: fk.page_alloc(one, counts, table, expected, tags, free_pages, free_count,
+                                                       status)),
+        "alloc_32x512_us": timed(lambda: fk.page_alloc(prefill, counts, table, expected, tags, free_pages,
+                                                         free_count, status)),
+    }
+
+    def alloc_then_free():
+        fk.page_alloc(prefill, counts, table, expected, tags, free_pages, free_count, status)
+        torch.cuda.synchronize(dev)
+    ms = []
+    for _ in range(reps):
+        fk.page_pool_init(free_pages, free_count)
+        counts.zero_()
+        alloc_then_free()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fk.page_free(release, counts, table, free_pages, free_count, status)
+        b.record()
+        torch.cuda.synchronize(dev)
+        ms.append(a.elapsed_time(b))
+    res["free_32x512_us"] = round(float(np.median(ms)) * 1e3, 2)
+    return res
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     for whole sequences taken in order, time one decode step (append of the new
@@ -424,6 +482,17 @@ def main():
         }
         if name == "fp8":
             res["tags"] = tag_overhead(case)
+            # the step's append, with the tag check of the page's owner
+            rs = torch.empty(w.new_k.shape[0], dtype=torch.uint8, device=dev)
+            nk, nv, ns, npos = case.new
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+            for a, b in evs:   # back to back like the step loop's appends
+                a.record()
+                fk.kv_quant_append_checked(nk, nv, ns, npos, case.pt, w.k_scale, w.v_scale, case.kc, case.vc,
+                                           case.tags, case.exp, rs)
+                b.record()
+            torch.cuda.synchronize(dev)
+            res["append_checked_us"] = float(np.median([a.elapsed_time(b) for a, b in evs])) * 1e3
         del case
         torch.cuda.empty_cache()
 
@@ -476,6 +545,8 @@ def main():
                               "protocol": "1 GiB read before each call (evicts the Infinity Cache), "
                                           "outside the timed region; 30 calls"},
         "append_32_rows_us": round(f["append_median_us"], 2),
+        "append_checked_32_rows_us": round(res["append_checked_us"], 2),
+        "page_pool": pool_timings(dev),
         "bulk_fill": f["fill"],
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }

@@ -20,6 +20,7 @@ __all__ = [
     "KV_FP8_E4M3", "KV_BF16", "ABORT_TAG_MISMATCH", "ABORT_BAD_METADATA", "Fp8KvError",
     "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
+    "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free",
 ]
 
 KV_FP8_E4M3 = 0
@@ -71,6 +72,15 @@ def load_library() -> ctypes.CDLL:
     lib.paged_decode_attn.restype = c.c_int
     lib.paged_decode_attn.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, vp, sz, i32, i32,
                                       i32, i32, i32, i32, f32, i32, vp]
+    lib.kv_quant_append_checked.restype = c.c_int
+    lib.kv_quant_append_checked.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, i32, i32, i32, i32,
+                                            i32, i32, vp, vp, vp, vp]
+    lib.page_pool_init.restype = c.c_int
+    lib.page_pool_init.argtypes = [vp, vp, i32, vp]
+    lib.page_alloc.restype = c.c_int
+    lib.page_alloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.page_free.restype = c.c_int
+    lib.page_free.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -181,3 +191,68 @@ def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flag
         batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_blocks),
         _stream_handle(dev, stream))
     _check("paged_decode_attn", status)
+
+
+def kv_quant_append_checked(k_new, v_new, row_seq, row_pos, page_table, k_scale, v_scale, k_cache, v_cache,
+                            page_tags, expected_tags, row_status, kv_dtype=KV_FP8_E4M3, stream=None):
+    """kv_quant_append that writes a row only if its page's tag still equals the
+    sequence's expected tag; ``row_status [n_rows]`` uint8 receives 0 written,
+    1 tag mismatch, 2 bad destination.  See ``kv_quant_append_checked`` in
+    ``include/fp8kv.h``."""
+    dev = k_cache.device
+    n_rows, hkv, d = k_new.shape
+    num_pages, hkv_c, page_size, d_c = k_cache.shape
+    if (hkv, d) != (hkv_c, d_c) or v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
+        raise ValueError("shape mismatch between rows and caches")
+    if row_seq.numel() != n_rows or row_pos.numel() != n_rows or row_status.numel() != n_rows:
+        raise ValueError("row_seq/row_pos/row_status must have n_rows entries")
+    batch, max_pages = page_table.shape
+    if page_tags.numel() != num_pages or tuple(expected_tags.shape) != (batch, max_pages):
+        raise ValueError("page_tags must be [num_pages] and expected_tags [batch, max_pages]")
+    status = load_library().kv_quant_append_checked(
+        _ptr(k_new, _BF16, "k_new", dev), _ptr(v_new, _BF16, "v_new", dev),
+        _ptr(row_seq, _I32, "row_seq", dev), _ptr(row_pos, _I32, "row_pos", dev),
+        _ptr(page_table, _I32, "page_table", dev), batch, max_pages, float(k_scale), float(v_scale),
+        _ptr(k_cache, _CACHE[kv_dtype], "k_cache", dev), _ptr(v_cache, _CACHE[kv_dtype], "v_cache", dev),
+        num_pages, n_rows, hkv, d, page_size, kv_dtype, _ptr(page_tags, _U32, "page_tags", dev),
+        _ptr(expected_tags, _U32, "expected_tags", dev), _ptr(row_status, (torch.uint8,), "row_status", dev),
+        _stream_handle(dev, stream))
+    _check("kv_quant_append_checked", status)
+
+
+def page_pool_init(free_pages, free_count, stream=None):
+    """Every page free: ``free_pages [num_pages]`` int32 stacked so pops return
+    0, 1, 2, ...; ``free_count [1]`` int32 = num_pages."""
+    dev = free_pages.device
+    status = load_library().page_pool_init(_ptr(free_pages, _I32, "free_pages", dev),
+                                           _ptr(free_count, _I32, "free_count", dev), free_pages.numel(),
+                                           _stream_handle(dev, stream))
+    _check("page_pool_init", status)
+
+
+def page_alloc(n_new, page_counts, page_table, expected_tags, page_tags, free_pages, free_count, status,
+               stream=None):
+    """Hand out pages (see ``page_alloc`` in ``include/fp8kv.h``); every argument
+    is a device tensor, updated in place."""
+    dev = page_table.device
+    batch, max_pages = page_table.shape
+    st = load_library().page_alloc(
+        _ptr(n_new, _I32, "n_new", dev), _ptr(page_counts, _I32, "page_counts", dev),
+        _ptr(page_table, _I32, "page_table", dev), _ptr(expected_tags, _U32, "expected_tags", dev),
+        _ptr(page_tags, _U32, "page_tags", dev), _ptr(free_pages, _I32, "free_pages", dev),
+        _ptr(free_count, _I32, "free_count", dev), _ptr(status, (torch.uint8,), "status", dev),
+        batch, max_pages, free_pages.numel(), _stream_handle(dev, stream))
+    _check("page_alloc", st)
+
+
+def page_free(release, page_counts, page_table, free_pages, free_count, status, stream=None):
+    """Return the pages of released sequences (see ``page_free`` in
+    ``include/fp8kv.h``)."""
+    dev = page_table.device
+    batch, max_pages = page_table.shape
+    st = load_library().page_free(
+        _ptr(release, (torch.uint8,), "release", dev), _ptr(page_counts, _I32, "page_counts", dev),
+        _ptr(page_table, _I32, "page_table", dev), _ptr(free_pages, _I32, "free_pages", dev),
+        _ptr(free_count, _I32, "free_count", dev), _ptr(status, (torch.uint8,), "status", dev),
+        batch, max_pages, free_pages.numel(), _stream_handle(dev, stream))
+    _check("page_free", st)

@@ -101,10 +101,12 @@ const char* fp8kv_status_string(int status) {
 
 const char* fp8kv_last_hip_error(void) { return g_last_hip_error; }
 
-int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
-                    const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
-                    void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* stream) {
+namespace {
+int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
+                      const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
+                      void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, int32_t kv_dtype, const uint32_t* page_tags,
+                      const uint32_t* expected_tags, uint8_t* row_status, void* stream) {
   if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
   if (n_rows < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
@@ -128,6 +130,9 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t*
   p.v_cache = v_cache;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.page_tags = page_tags;
+  p.expected_tags = expected_tags;
+  p.row_status = row_status;
   p.batch = batch;
   p.max_pages = max_pages;
   p.num_pages = num_pages;
@@ -136,6 +141,78 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t*
   p.head_dim = head_dim;
   p.log2_page_size = l2ps;
   return record_hip(launch_quant_append(p, kv_dtype, static_cast<hipStream_t>(stream)));
+}
+
+bool pool_sizes_ok(int32_t batch, int32_t max_pages, int32_t num_pages) {
+  return batch > 0 && max_pages > 0 && num_pages > 0;
+}
+}  // namespace
+
+int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
+                    const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
+                    void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* stream) {
+  return quant_append_impl(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, k_scale, v_scale, k_cache,
+                           v_cache, num_pages, n_rows, num_kv_heads, head_dim, page_size, kv_dtype, nullptr,
+                           nullptr, nullptr, stream);
+}
+
+int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq,
+                            const int32_t* row_pos, const int32_t* page_table, int32_t batch, int32_t max_pages,
+                            float k_scale, float v_scale, void* k_cache, void* v_cache, int32_t num_pages,
+                            int32_t n_rows, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                            int32_t kv_dtype, const uint32_t* page_tags, const uint32_t* expected_tags,
+                            uint8_t* row_status, void* stream) {
+  if (n_rows > 0 && (!page_tags || !expected_tags || !row_status)) return FP8KV_ERR_NULL;
+  return quant_append_impl(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, k_scale, v_scale, k_cache,
+                           v_cache, num_pages, n_rows, num_kv_heads, head_dim, page_size, kv_dtype, page_tags,
+                           expected_tags, row_status, stream);
+}
+
+int page_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, void* stream) {
+  if (num_pages <= 0) return FP8KV_ERR_SHAPE;
+  if (!free_pages || !free_count) return FP8KV_ERR_NULL;
+  return record_hip(launch_pool_init(free_pages, free_count, num_pages, static_cast<hipStream_t>(stream)));
+}
+
+int page_alloc(const int32_t* n_new, int32_t* page_counts, int32_t* page_table, uint32_t* expected_tags,
+               uint32_t* page_tags, int32_t* free_pages, int32_t* free_count, uint8_t* status, int32_t batch,
+               int32_t max_pages, int32_t num_pages, void* stream) {
+  if (!pool_sizes_ok(batch, max_pages, num_pages)) return FP8KV_ERR_SHAPE;
+  if (!n_new || !page_counts || !page_table || !expected_tags || !page_tags || !free_pages || !free_count ||
+      !status)
+    return FP8KV_ERR_NULL;
+  PoolParams p{};
+  p.n_new = n_new;
+  p.page_counts = page_counts;
+  p.page_table = page_table;
+  p.expected_tags = expected_tags;
+  p.page_tags = page_tags;
+  p.free_pages = free_pages;
+  p.free_count = free_count;
+  p.status = status;
+  p.batch = batch;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  return record_hip(launch_pool_alloc(p, static_cast<hipStream_t>(stream)));
+}
+
+int page_free(const uint8_t* release, int32_t* page_counts, const int32_t* page_table, int32_t* free_pages,
+              int32_t* free_count, uint8_t* status, int32_t batch, int32_t max_pages, int32_t num_pages,
+              void* stream) {
+  if (!pool_sizes_ok(batch, max_pages, num_pages)) return FP8KV_ERR_SHAPE;
+  if (!release || !page_counts || !page_table || !free_pages || !free_count || !status) return FP8KV_ERR_NULL;
+  PoolParams p{};
+  p.release = release;
+  p.page_counts = page_counts;
+  p.page_table = const_cast<int32_t*>(page_table);  // only read by the free kernel
+  p.free_pages = free_pages;
+  p.free_count = free_count;
+  p.status = status;
+  p.batch = batch;
+  p.max_pages = max_pages;
+  p.num_pages = num_pages;
+  return record_hip(launch_pool_free(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

@@ -22,7 +22,23 @@ struct AppendParams {
   void* k_cache;
   void* v_cache;
   float k_scale, v_scale;
+  const uint32_t* page_tags;        // checked append: [num_pages], or null (no check)
+  const uint32_t* expected_tags;    // checked append: [B][max_pages]
+  uint8_t* row_status;              // checked append: [n_rows] 0 written, 1 tag mismatch, 2 bad destination
   int32_t batch, max_pages, num_pages, n_rows, num_kv_heads, head_dim, log2_page_size;
+};
+
+struct PoolParams {
+  const int32_t* n_new;             // alloc: pages requested per sequence [B]
+  const uint8_t* release;           // free: nonzero = return the sequence's pages [B]
+  int32_t* page_counts;             // [B] pages each sequence holds
+  int32_t* page_table;              // [B][max_pages]
+  uint32_t* expected_tags;          // [B][max_pages]
+  uint32_t* page_tags;              // [num_pages]
+  int32_t* free_pages;              // [num_pages] stack of free page ids (top = last)
+  int32_t* free_count;              // [1] number of free pages
+  uint8_t* status;                  // [B]
+  int32_t batch, max_pages, num_pages;
 };
 
 struct DecodeParams {
@@ -60,6 +76,9 @@ constexpr int32_t kCheckSlots = 1024;  // page-table slots per page-check block
 inline int32_t check_chunks(int32_t max_pages) { return (max_pages + kCheckSlots - 1) / kCheckSlots; }
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream);
+hipError_t launch_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, hipStream_t stream);
+hipError_t launch_pool_alloc(const PoolParams& p, hipStream_t stream);
+hipError_t launch_pool_free(const PoolParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,
                          hipStream_t stream);
 

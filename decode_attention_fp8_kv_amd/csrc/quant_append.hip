@@ -49,9 +49,24 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
   const int seq = p.row_seq[row];
   const int pos = p.row_pos[row];
   const int page_size = 1 << p.log2_page_size;
-  if (seq < 0 || seq >= p.batch || pos < 0 || pos >= p.max_pages * page_size) return;
-  const int page = p.page_table[(int64_t)seq * p.max_pages + (pos >> p.log2_page_size)];
-  if (page < 0 || page >= p.num_pages) return;
+  const bool reports = p.row_status != nullptr && e0 == 0;  // the row's first thread reports its status
+  if (seq < 0 || seq >= p.batch || pos < 0 || pos >= p.max_pages * page_size) {
+    if (reports) p.row_status[row] = 2;
+    return;
+  }
+  const int64_t at = (int64_t)seq * p.max_pages + (pos >> p.log2_page_size);
+  const int page = p.page_table[at];
+  if (page < 0 || page >= p.num_pages) {
+    if (reports) p.row_status[row] = 2;
+    return;
+  }
+  // Checked append: the page must still belong to the generation the
+  // sequence recorded for this slot.
+  if (p.page_tags != nullptr && p.page_tags[page] != p.expected_tags[at]) {
+    if (reports) p.row_status[row] = 1;
+    return;
+  }
+  if (reports) p.row_status[row] = 0;
   const int slot = pos & (page_size - 1);
   const int64_t dst = (((int64_t)page * p.num_kv_heads + head) * page_size + slot) * p.head_dim + d0;
   const int64_t src = (int64_t)row * p.num_kv_heads * p.head_dim + e0;

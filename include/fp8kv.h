@@ -119,6 +119,86 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                     int32_t page_size, int32_t kv_dtype, void* stream);
 
 /*
+ * kv_quant_append_checked -- kv_quant_append that writes a row only while
+ * its page still belongs to the generation the sequence recorded: a row is
+ * written iff page_tags[p] == expected_tags[seq * max_pages + pos /
+ * page_size] for its page p.  Same arguments as kv_quant_append plus
+ *
+ *   page_tags      uint32 [num_pages]              current page generations
+ *   expected_tags  uint32 [batch][max_pages]       generations the sequences
+ *                  recorded (written by page_alloc)
+ *   row_status     uint8 [n_rows] (written): 0 written, 1 tag mismatch (not
+ *                  written), 2 destination out of range (not written)
+ *
+ * For the writer side of the tag check: an append through a stale page
+ * table (its pages freed and handed to another sequence) is refused instead
+ * of overwriting the new owner's data ("ترفندهای کلادفلر برای جا دادن
+ * مدل‌های غول‌پیکر تو GPU", third technique).  Errors: as kv_quant_append;
+ * FP8KV_ERR_NULL if a tag or status pointer is NULL.
+ */
+int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new,
+                            const int32_t* row_seq, const int32_t* row_pos,
+                            const int32_t* page_table, int32_t batch, int32_t max_pages,
+                            float k_scale, float v_scale,
+                            void* k_cache, void* v_cache, int32_t num_pages,
+                            int32_t n_rows, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t kv_dtype,
+                            const uint32_t* page_tags, const uint32_t* expected_tags,
+                            uint8_t* row_status, void* stream);
+
+/*
+ * Generation-tagged page pool ("ترفندهای کلادفلر برای جا دادن مدل‌های
+ * غول‌پیکر تو GPU", third technique; "Tối ưu hóa mô hình AI quy mô lớn",
+ * section "Bảo vệ tính toàn vẹn của KV Cache": a page's tag changes whenever
+ * the page is handed to a new owner).  All state lives in device memory,
+ * owned by the caller; every call is one kernel on `stream`, deterministic.
+ *
+ *   free_pages     int32 [num_pages]  stack of free page ids (top = the
+ *                  entry at free_count - 1)
+ *   free_count     int32 [1]          number of free pages
+ *   page_counts    int32 [batch]      pages each sequence holds (its first
+ *                  page_counts[b] table entries)
+ *   page_table     int32 [batch][max_pages]
+ *   expected_tags  uint32 [batch][max_pages]
+ *   page_tags      uint32 [num_pages]
+ *
+ * page_pool_init: every page free, stacked so that pops return 0, 1, 2, ...
+ * (tags are left as they are).
+ *
+ * page_alloc: sequence b asks for n_new[b] more pages.  Valid iff n_new[b]
+ * >= 0 and 0 <= page_counts[b] <= page_counts[b] + n_new[b] <= max_pages
+ * (else status 2, nothing changes for b).  Valid requests are served in
+ * order of b while their running total fits: b is served iff (sum of the
+ * valid requests before b) + n_new[b] <= free_count (else status 1); a
+ * request for zero pages is always served (status 0).  A served request
+ * pops its pages in order into its next table slots; each page's tag is
+ * incremented (mod 2^32) and the new value recorded in expected_tags.  A
+ * popped id outside [0, num_pages) (a corrupt stack) is recorded as is with
+ * expected tag 0 and no tag write -- the decode's page check flags it.
+ *
+ * page_free: every sequence with release[b] != 0 pushes its pages back in
+ * order of b, then slot, and then holds 0 pages (status 0); page_counts[b]
+ * outside [0, max_pages] is status 2; pushes are served in order while they
+ * fit in the stack (else status 1), so a double free cannot overflow it.
+ * Tags do not change on free; the released rows of page_table and
+ * expected_tags are left as they were, so a reader still using them fails
+ * the tag check once a page has a new owner.  status[b] = 0 for sequences
+ * not released.
+ *
+ * Errors: FP8KV_ERR_SHAPE (batch, max_pages or num_pages <= 0),
+ * FP8KV_ERR_NULL; device-side conditions are status codes, never errors.
+ * Calls that share a pool must be ordered (same stream).
+ */
+int page_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, void* stream);
+int page_alloc(const int32_t* n_new, int32_t* page_counts, int32_t* page_table,
+               uint32_t* expected_tags, uint32_t* page_tags,
+               int32_t* free_pages, int32_t* free_count, uint8_t* status,
+               int32_t batch, int32_t max_pages, int32_t num_pages, void* stream);
+int page_free(const uint8_t* release, int32_t* page_counts, const int32_t* page_table,
+              int32_t* free_pages, int32_t* free_count, uint8_t* status,
+              int32_t batch, int32_t max_pages, int32_t num_pages, void* stream);
+
+/*
  * paged_decode_attn_workspace_size -- bytes of device workspace that
  * paged_decode_attn needs for these sizes (a multiple of 256; mostly
  * 2 * 4 * num_blocks partial slots of 4 * G * (head_dim + 2) bytes each,

@@ -26,9 +26,16 @@ allocator; the readings taken here (plainest ones consistent with that):
   incremented (mod 2^32) -- the page changes owner, so its generation
   changes -- and the new tag is recorded as the sequence's expected tag for
   that slot.
+* A popped id outside [0, num_pages) (a corrupt stack) is recorded as is,
+  with expected tag 0 and no tag change; the decode's page check then
+  flags it.
 * ``free``: every sequence with release[b] != 0 pushes its pages back, in
-  order of b then slot, and holds 0 pages afterwards.  Tags do not change
-  on free (they change when the page is handed out again); the freed
+  order of b then slot, and holds 0 pages afterwards (status 0).  A count
+  outside [0, max_pages] is status 2 (nothing happens).  Like alloc, the
+  pushes are a prefix: sequence b is pushed iff free_count + (pages of the
+  valid released sequences before b) + its count <= num_pages (else status
+  1), so a double free can never overflow the stack.  Tags do not change on
+  free (they change when the page is handed out again); the freed
   sequence's table row is left as it was, so a reader that still uses it
   fails the tag check once the page has a new owner.
 * ``append_checked``: kv_quant_append that writes a row only if its page's
@@ -49,6 +56,10 @@ ALLOC_OK = 0
 ALLOC_NO_PAGES = 1
 ALLOC_BAD_REQUEST = 2
 
+FREE_OK = 0
+FREE_STACK_FULL = 1
+FREE_BAD_COUNT = 2
+
 ROW_WRITTEN = 0
 ROW_TAG_MISMATCH = 1
 ROW_BAD_DESTINATION = 2
@@ -64,6 +75,7 @@ def alloc(n_new, page_counts, page_table, expected_tags, page_tags, free_pages, 
     """Serve page requests in order (see module docstring).  Updates the
     arrays in place; returns (status uint8 [batch], new free_count)."""
     batch, max_pages = page_table.shape
+    free_count = min(max(int(free_count), 0), len(free_pages))  # a count outside the stack is clamped
     status = np.zeros(batch, np.uint8)
     valid = []
     for b in range(batch):
@@ -86,29 +98,46 @@ def alloc(n_new, page_counts, page_table, expected_tags, page_tags, free_pages, 
         r, c = int(n_new[b]), int(page_counts[b])
         for k in range(r):
             p = int(free_pages[free_count - 1 - (start + k)])
-            page_tags[p] = np.uint32((int(page_tags[p]) + 1) & 0xFFFFFFFF)
             page_table[b, c + k] = p
-            expected_tags[b, c + k] = page_tags[p]
+            if 0 <= p < len(page_tags):
+                page_tags[p] = np.uint32((int(page_tags[p]) + 1) & 0xFFFFFFFF)
+                expected_tags[b, c + k] = page_tags[p]
+            else:
+                expected_tags[b, c + k] = 0
         page_counts[b] = c + r
         taken += r
     return status, free_count - taken
 
 
 def free(release, page_counts, page_table, free_pages, free_count):
-    """Return the pages of every released sequence; returns the new free_count."""
+    """Return the pages of every released sequence (see module docstring).
+    Updates the arrays in place; returns (status uint8 [batch], new free_count)."""
     batch, max_pages = page_table.shape
-    top = free_count
+    num_pages = len(free_pages)
+    free_count = min(max(int(free_count), 0), num_pages)  # a count outside the stack is clamped
+    status = np.zeros(batch, np.uint8)
+    before = 0
+    pushed = []
     for b in range(batch):
         if not release[b]:
             continue
         c = int(page_counts[b])
         if c < 0 or c > max_pages:
-            continue  # a corrupt count is left alone
+            status[b] = FREE_BAD_COUNT
+            continue
+        if free_count + before + c <= num_pages:
+            pushed.append((b, before))
+        else:
+            status[b] = FREE_STACK_FULL
+        before += c
+    top = free_count
+    for b, start in pushed:
+        c = int(page_counts[b])
         for k in range(c):
-            free_pages[top] = page_table[b, k]
-            top += 1
+            free_pages[free_count + start + k] = page_table[b, k]
         page_counts[b] = 0
-    return top
+        top += c
+    return status, top
 
 
 def append_checked(k_new, v_new, row_seq, row_pos, page_table, page_tags, expected_tags, k_scale, v_scale,

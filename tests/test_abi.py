@@ -157,3 +157,22 @@ def test_path_selection(lib, monkeypatch):
     monkeypatch.setenv("FP8KV_FORCE_PATH", "valu")
     assert fk.paged_decode_attn_path(8, 2) == 0
     assert fk.paged_decode_attn_path(64, 8) == 1      # VALU covers groups up to 4 only
+
+
+def test_pool_and_checked_append_validation_codes(lib):
+    E = {n: _header_define("FP8KV_ERR_" + n) for n in ["NULL", "SHAPE"]}
+    assert lib.page_pool_init(None, FAKE, 8, None) == E["NULL"]
+    assert lib.page_pool_init(FAKE, FAKE, 0, None) == E["SHAPE"]
+    args = [FAKE] * 8
+    assert lib.page_alloc(*args, 0, 4, 8, None) == E["SHAPE"]
+    assert lib.page_alloc(*args, 2, 4, 0, None) == E["SHAPE"]
+    assert lib.page_alloc(None, *args[1:], 2, 4, 8, None) == E["NULL"]
+    assert lib.page_alloc(*args[:7], None, 2, 4, 8, None) == E["NULL"]
+    args = [FAKE] * 6
+    assert lib.page_free(*args, 2, 0, 8, None) == E["SHAPE"]
+    assert lib.page_free(*args[:5], None, 2, 4, 8, None) == E["NULL"]
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 1.0, 1.0, FAKE, FAKE, 64, 4, 2, 64, 16, 0]
+    assert lib.kv_quant_append_checked(*base, None, FAKE, FAKE, None) == E["NULL"]
+    assert lib.kv_quant_append_checked(*base, FAKE, FAKE, None, None) == E["NULL"]
+    base[12] = 0  # no rows: nothing to check, nothing launched
+    assert lib.kv_quant_append_checked(*base, None, None, None, None) == 0

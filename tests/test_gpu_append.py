@@ -82,9 +82,7 @@ def test_append_fp8_all_bf16_patterns_many_scales(gpu_device, scale):
     kc = torch.full(shape, 0xA5, dtype=torch.uint8, device=gpu_device)
     vc = torch.full(shape, 0x5A, dtype=torch.uint8, device=gpu_device)
     vt = torch.flip(t.view(-1), [0]).view(t.shape).contiguous()
-    v_scale = float(np.float32(scale * 1.37))
-    if not np.isfinite(v_scale) or v_scale <= 0:
-        v_scale = scale
+    v_scale = float(np.float32(min(scale * 1.37, 3.0e38)))
     fk.kv_quant_append(t.to(gpu_device), vt.to(gpu_device), torch.from_numpy(seq).to(gpu_device),
                        torch.from_numpy(pos).to(gpu_device), torch.from_numpy(pt).to(gpu_device),
                        scale, v_scale, kc, vc, fk.KV_FP8_E4M3)

@@ -23,8 +23,9 @@ def _alloc(P, n_new):
 
 
 def _free(P, release):
-    P["free_count"] = pp.free(np.asarray(release, np.uint8), P["counts"], P["table"], P["free_pages"],
-                              P["free_count"])
+    st, P["free_count"] = pp.free(np.asarray(release, np.uint8), P["counts"], P["table"], P["free_pages"],
+                                  P["free_count"])
+    return st
 
 
 def test_fresh_pool_pops_in_id_order():
@@ -127,6 +128,29 @@ def test_use_after_free_is_caught_by_decode_and_by_checked_append():
     st = pp.append_checked(rows[:1], rows[:1], np.array([5]), np.array([0]), table, P["tags"], expected,
                            1.0, 1.0, kc, vc)
     assert list(st) == [pp.ROW_BAD_DESTINATION]
+
+
+def test_free_rules_bad_count_and_full_stack():
+    P = _pool(3, 4, 6)
+    _alloc(P, [2, 2, 2])                          # all 6 pages out
+    P["counts"][1] = 7                            # corrupt count
+    st = _free(P, [1, 1, 0])
+    assert list(st) == [pp.FREE_OK, pp.FREE_BAD_COUNT, pp.FREE_OK]
+    assert P["free_count"] == 2 and P["counts"].tolist() == [0, 7, 2]
+    # a double free cannot overflow the stack: pretend seq 2's pages were already returned
+    P["free_count"] = 5
+    st = _free(P, [0, 0, 1])                      # 5 + 2 > 6 -> refused, nothing written
+    assert list(st) == [0, 0, pp.FREE_STACK_FULL] and P["free_count"] == 5 and P["counts"][2] == 2
+
+
+def test_corrupt_stack_entry_is_recorded_without_tag_write():
+    P = _pool(1, 2, 2)
+    P["free_pages"][1] = 9                         # top of the stack (next pop) holds an id outside the pool
+    st = _alloc(P, [2])                           # pops 9, then page 1
+    assert list(st) == [0] and list(P["table"][0]) == [9, 1]
+    assert list(P["expected"][0]) == [0, 1] and list(P["tags"]) == [0, 1]
+    flags = pa.abort_flags(P["table"], np.array([32]), 16, 2, P["tags"], P["expected"])
+    assert list(flags) == [pa.ABORT_BAD_METADATA]
 
 
 def test_tag_wraps_mod_2_32():
