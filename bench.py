@@ -274,6 +274,40 @@ def pool_timings(dev, batch=32, max_pages=513, reps=20):
     return res
 
 
+def handoff_timings(dev, reps=10):
+    """Prefill -> decode hand-off of a 32,768-token prefill (64/8 heads, head_dim
+    128, 64-token pages): device amax + scale of K and of V, then the
+    device-scale append into the FP8 pool.  Median of `reps` after a warm-up;
+    GB/s at 2 bytes per element read (amax) and 3 per element (append)."""
+    import torch
+    import decode_attention_fp8_kv_amd as fk
+    from decode_attention_fp8_kv_amd import workloads as W
+
+    w = W.make("latency", device=dev)
+    k, v = w.ctx_k.contiguous(), w.ctx_v.contiguous()
+    shape = (w.num_pages, w.num_kv_heads, w.page_size, w.head_dim)
+    kc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    vc = torch.empty(shape, dtype=torch.uint8, device=dev)
+    pt = torch.from_numpy(w.page_table).to(dev)
+    ks, vs = torch.zeros(4, device=dev), torch.zeros(4, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
+    for e in ev:
+        e[0].record()
+        fk.kv_absmax_scale(k, ks)
+        fk.kv_absmax_scale(v, vs)
+        e[1].record()
+        fk.kv_quant_append_dscale(k, v, w.ctx_seq, w.ctx_pos, pt, ks[1:2], vs[1:2], kc, vc)
+        e[2].record()
+    torch.cuda.synchronize(dev)
+    amax_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev[2:]]))
+    app_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev[2:]]))
+    n = k.numel() + v.numel()
+    return {"tokens": int(k.shape[0]), "amax_scale_us": round(amax_ms * 1e3, 1),
+            "amax_gbps": round(2 * n / (amax_ms * 1e-3) / 1e9, 1), "append_us": round(app_ms * 1e3, 1),
+            "append_gbps": round(3 * n / (app_ms * 1e-3) / 1e9, 1),
+            "total_us": round((amax_ms + app_ms) * 1e3, 1)}
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     for whole sequences taken in order, time one decode step (append of the new
@@ -547,6 +581,7 @@ def main():
         "append_32_rows_us": round(f["append_median_us"], 2),
         "append_checked_32_rows_us": round(res["append_checked_us"], 2),
         "page_pool": pool_timings(dev),
+        "prefill_handoff": handoff_timings(dev),
         "bulk_fill": f["fill"],
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }

@@ -20,7 +20,8 @@ __all__ = [
     "KV_FP8_E4M3", "KV_BF16", "ABORT_TAG_MISMATCH", "ABORT_BAD_METADATA", "Fp8KvError",
     "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
-    "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free",
+    "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free", "kv_absmax_scale",
+    "kv_quant_append_dscale",
 ]
 
 KV_FP8_E4M3 = 0
@@ -75,6 +76,11 @@ def load_library() -> ctypes.CDLL:
     lib.kv_quant_append_checked.restype = c.c_int
     lib.kv_quant_append_checked.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, i32, i32, i32, i32,
                                             i32, i32, vp, vp, vp, vp]
+    lib.kv_absmax_scale.restype = c.c_int
+    lib.kv_absmax_scale.argtypes = [vp, c.c_int64, vp, vp]
+    lib.kv_quant_append_dscale.restype = c.c_int
+    lib.kv_quant_append_dscale.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                           vp]
     lib.page_pool_init.restype = c.c_int
     lib.page_pool_init.argtypes = [vp, vp, i32, vp]
     lib.page_alloc.restype = c.c_int
@@ -256,3 +262,38 @@ def page_free(release, page_counts, page_table, free_pages, free_count, status, 
         _ptr(free_count, _I32, "free_count", dev), _ptr(status, (torch.uint8,), "status", dev),
         batch, max_pages, free_pages.numel(), _stream_handle(dev, stream))
     _check("page_free", st)
+
+
+def kv_absmax_scale(x, out, stream=None):
+    """``out[0]`` = max |x| over the finite elements of the bf16 tensor ``x``,
+    ``out[1]`` = out[0] / 448 (1 if out[0] is 0); ``out`` is a float32 [4]
+    device tensor whose last two elements are zero before the first call
+    (``torch.zeros(4)``; every call leaves them zero).  See
+    ``kv_absmax_scale`` in ``include/fp8kv.h``."""
+    dev = x.device
+    if out.dtype != torch.float32 or out.numel() < 4:
+        raise ValueError("out must be a float32 tensor with 4 elements")
+    st = load_library().kv_absmax_scale(_ptr(x, _BF16, "x", dev), x.numel(),
+                                        _ptr(out, (torch.float32,), "out", dev), _stream_handle(dev, stream))
+    _check("kv_absmax_scale", st)
+
+
+def kv_quant_append_dscale(k_new, v_new, row_seq, row_pos, page_table, k_scale_dev, v_scale_dev, k_cache,
+                           v_cache, stream=None):
+    """kv_quant_append into an FP8 cache with the scales read from device
+    memory: ``k_scale_dev`` / ``v_scale_dev`` are float32 device tensors whose
+    first element is the scale (e.g. ``out[1:]`` of kv_absmax_scale)."""
+    dev = k_cache.device
+    n_rows, hkv, d = k_new.shape
+    num_pages, hkv_c, page_size, d_c = k_cache.shape
+    if (hkv, d) != (hkv_c, d_c) or v_cache.shape != k_cache.shape or v_new.shape != k_new.shape:
+        raise ValueError("shape mismatch between rows and caches")
+    batch, max_pages = page_table.shape
+    st = load_library().kv_quant_append_dscale(
+        _ptr(k_new, _BF16, "k_new", dev), _ptr(v_new, _BF16, "v_new", dev),
+        _ptr(row_seq, _I32, "row_seq", dev), _ptr(row_pos, _I32, "row_pos", dev),
+        _ptr(page_table, _I32, "page_table", dev), batch, max_pages,
+        k_scale_dev.data_ptr(), v_scale_dev.data_ptr(),
+        _ptr(k_cache, _CACHE[KV_FP8_E4M3], "k_cache", dev), _ptr(v_cache, _CACHE[KV_FP8_E4M3], "v_cache", dev),
+        num_pages, n_rows, hkv, d, page_size, _stream_handle(dev, stream))
+    _check("kv_quant_append_dscale", st)

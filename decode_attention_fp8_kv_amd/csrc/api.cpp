@@ -106,7 +106,8 @@ int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_
                       const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
                       void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
                       int32_t head_dim, int32_t page_size, int32_t kv_dtype, const uint32_t* page_tags,
-                      const uint32_t* expected_tags, uint8_t* row_status, void* stream) {
+                      const uint32_t* expected_tags, uint8_t* row_status, const float* k_scale_dev,
+                      const float* v_scale_dev, void* stream) {
   if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
   if (n_rows < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
@@ -115,12 +116,14 @@ int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_
   if ((int64_t)max_pages * page_size > INT32_MAX) return FP8KV_ERR_SHAPE;
   if (n_rows == 0) return FP8KV_OK;
   if (!k_new || !v_new || !row_seq || !row_pos || !page_table || !k_cache || !v_cache) return FP8KV_ERR_NULL;
-  if (kv_dtype == FP8KV_KV_FP8_E4M3 && (!finite_positive(k_scale) || !finite_positive(v_scale)))
+  if (kv_dtype == FP8KV_KV_FP8_E4M3 && !k_scale_dev && (!finite_positive(k_scale) || !finite_positive(v_scale)))
     return FP8KV_ERR_SCALE;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return FP8KV_ERR_ALIGN;
 
   AppendParams p;
+  p.k_scale_dev = k_scale_dev;
+  p.v_scale_dev = v_scale_dev;
   p.k_new = k_new;
   p.v_new = v_new;
   p.row_seq = row_seq;
@@ -154,7 +157,7 @@ int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new, const int32_t*
                     int32_t head_dim, int32_t page_size, int32_t kv_dtype, void* stream) {
   return quant_append_impl(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, k_scale, v_scale, k_cache,
                            v_cache, num_pages, n_rows, num_kv_heads, head_dim, page_size, kv_dtype, nullptr,
-                           nullptr, nullptr, stream);
+                           nullptr, nullptr, nullptr, nullptr, stream);
 }
 
 int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq,
@@ -166,7 +169,26 @@ int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new, const 
   if (n_rows > 0 && (!page_tags || !expected_tags || !row_status)) return FP8KV_ERR_NULL;
   return quant_append_impl(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, k_scale, v_scale, k_cache,
                            v_cache, num_pages, n_rows, num_kv_heads, head_dim, page_size, kv_dtype, page_tags,
-                           expected_tags, row_status, stream);
+                           expected_tags, row_status, nullptr, nullptr, stream);
+}
+
+int kv_quant_append_dscale(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq,
+                           const int32_t* row_pos, const int32_t* page_table, int32_t batch, int32_t max_pages,
+                           const float* k_scale_dev, const float* v_scale_dev, void* k_cache, void* v_cache,
+                           int32_t num_pages, int32_t n_rows, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, void* stream) {
+  if (n_rows > 0 && (!k_scale_dev || !v_scale_dev)) return FP8KV_ERR_NULL;
+  if (n_rows > 0 && (!aligned(k_scale_dev, 4) || !aligned(v_scale_dev, 4))) return FP8KV_ERR_ALIGN;
+  return quant_append_impl(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, 1.0f, 1.0f, k_cache,
+                           v_cache, num_pages, n_rows, num_kv_heads, head_dim, page_size, FP8KV_KV_FP8_E4M3,
+                           nullptr, nullptr, nullptr, k_scale_dev, v_scale_dev, stream);
+}
+
+int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, void* stream) {
+  if (n < 0) return FP8KV_ERR_SHAPE;
+  if (!out || (n > 0 && !x)) return FP8KV_ERR_NULL;
+  if ((n > 0 && !aligned(x, 16)) || !aligned(out, 16)) return FP8KV_ERR_ALIGN;
+  return record_hip(launch_absmax_scale(x, n, out, static_cast<hipStream_t>(stream)));
 }
 
 int page_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, void* stream) {

@@ -22,6 +22,8 @@ struct AppendParams {
   void* k_cache;
   void* v_cache;
   float k_scale, v_scale;
+  const float* k_scale_dev;         // device-scale append: scales read from device memory, or null
+  const float* v_scale_dev;
   const uint32_t* page_tags;        // checked append: [num_pages], or null (no check)
   const uint32_t* expected_tags;    // checked append: [B][max_pages]
   uint8_t* row_status;              // checked append: [n_rows] 0 written, 1 tag mismatch, 2 bad destination
@@ -76,6 +78,7 @@ constexpr int32_t kCheckSlots = 1024;  // page-table slots per page-check block
 inline int32_t check_chunks(int32_t max_pages) { return (max_pages + kCheckSlots - 1) / kCheckSlots; }
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream);
+hipError_t launch_absmax_scale(const uint16_t* x, int64_t n, float* out, hipStream_t stream);
 hipError_t launch_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, hipStream_t stream);
 hipError_t launch_pool_alloc(const PoolParams& p, hipStream_t stream);
 hipError_t launch_pool_free(const PoolParams& p, hipStream_t stream);

@@ -78,8 +78,13 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
     vin[h] = *reinterpret_cast<const u32x4_t*>(p.v_new + src + 8 * h);
   }
   if constexpr (KV == 0) {
-    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = quant16(kin, p.k_scale);
-    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = quant16(vin, p.v_scale);
+    // Device-scale append: the scales come from device memory (a scale that
+    // is not finite and positive writes nothing).
+    const float ks = p.k_scale_dev != nullptr ? *p.k_scale_dev : p.k_scale;
+    const float vs = p.v_scale_dev != nullptr ? *p.v_scale_dev : p.v_scale;
+    if (!(ks > 0.f && ks <= 3.40282347e38f && vs > 0.f && vs <= 3.40282347e38f)) return;
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = quant16(kin, ks);
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = quant16(vin, vs);
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {

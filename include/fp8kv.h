@@ -147,6 +147,38 @@ int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new,
                             uint8_t* row_status, void* stream);
 
 /*
+ * Prefill -> decode hand-off ("Cloudflare tối ưu hóa Kimi và GLM trên
+ * Workers AI", section "Lượng tử hóa KV cache": prefill keeps BF16, decode
+ * reads the FP8 cache, so a prefill's K/V are converted once when handed
+ * over).  Reading of the scale rule (the pages give none): one fp32 scale
+ * per tensor that maps the largest finite magnitude onto e4m3's 448.
+ *
+ * kv_absmax_scale -- out[0] = max |x| over the finite elements of the BF16
+ * tensor x [n] (NaNs and infinities ignored; 0 if there are none), out[1] =
+ * out[0] / 448 (IEEE fp32 division), or 1 if out[0] is 0.  out is a device
+ * buffer of 4 floats (16-byte aligned): out[2] is the reduction's state,
+ * which must be ZERO BEFORE THE FIRST CALL (every call leaves it zero), and
+ * out[3] is unused.  Calls sharing an out buffer must be ordered (same
+ * stream).  x is 16-byte aligned.  Two kernels on `stream`.  Errors:
+ * FP8KV_ERR_SHAPE (n < 0), FP8KV_ERR_NULL, FP8KV_ERR_ALIGN.
+ *
+ * kv_quant_append_dscale -- kv_quant_append into an FP8 cache with the
+ * scales read from device memory (e.g. out + 1 of kv_absmax_scale), so the
+ * hand-off needs no host round trip.  A scale that is not finite and
+ * positive writes nothing (there is no host check to reject it).  Errors as
+ * kv_quant_append (no FP8KV_ERR_SCALE), plus FP8KV_ERR_NULL / _ALIGN for the
+ * scale pointers (4-byte aligned).
+ */
+int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, void* stream);
+int kv_quant_append_dscale(const uint16_t* k_new, const uint16_t* v_new,
+                           const int32_t* row_seq, const int32_t* row_pos,
+                           const int32_t* page_table, int32_t batch, int32_t max_pages,
+                           const float* k_scale_dev, const float* v_scale_dev,
+                           void* k_cache, void* v_cache, int32_t num_pages,
+                           int32_t n_rows, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t page_size, void* stream);
+
+/*
  * Generation-tagged page pool ("ترفندهای کلادفلر برای جا دادن مدل‌های
  * غول‌پیکر تو GPU", third technique; "Tối ưu hóa mô hình AI quy mô lớn",
  * section "Bảo vệ tính toàn vẹn của KV Cache": a page's tag changes whenever

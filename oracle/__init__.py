@@ -30,9 +30,10 @@ Modules:
 * ``oracle.paged_attn`` -- append scatter, tag/abort rule, fp64 attention.
 * ``oracle.page_pool``  -- generation-tagged page allocator (alloc/free) and
   the tag-checked append.
+* ``oracle.scale``      -- per-tensor amax and scale for the prefill hand-off.
 
 Parity pins for every function live in ``tests/test_oracle_*.py``; no
 function here is "parity unpinned".
 """
 
-from . import e4m3, page_pool, paged_attn  # noqa: F401
+from . import e4m3, page_pool, paged_attn, scale  # noqa: F401

@@ -176,3 +176,16 @@ def test_pool_and_checked_append_validation_codes(lib):
     assert lib.kv_quant_append_checked(*base, FAKE, FAKE, None, None) == E["NULL"]
     base[12] = 0  # no rows: nothing to check, nothing launched
     assert lib.kv_quant_append_checked(*base, None, None, None, None) == 0
+
+
+def test_handoff_validation_codes(lib):
+    E = {n: _header_define("FP8KV_ERR_" + n) for n in ["NULL", "SHAPE", "ALIGN"]}
+    assert lib.kv_absmax_scale(FAKE, -1, FAKE, None) == E["SHAPE"]
+    assert lib.kv_absmax_scale(None, 8, FAKE, None) == E["NULL"]
+    assert lib.kv_absmax_scale(FAKE, 8, None, None) == E["NULL"]
+    assert lib.kv_absmax_scale(FAKE + 2, 8, FAKE, None) == E["ALIGN"]
+    assert lib.kv_absmax_scale(FAKE, 8, FAKE + 8, None) == E["ALIGN"]
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8]
+    tail = [FAKE, FAKE, 64, 4, 2, 64, 16, None]
+    assert lib.kv_quant_append_dscale(*base, None, FAKE, *tail) == E["NULL"]
+    assert lib.kv_quant_append_dscale(*base, FAKE, FAKE + 2, *tail) == E["ALIGN"]
