@@ -289,12 +289,13 @@ def handoff_timings(dev, reps=10):
     kc = torch.empty(shape, dtype=torch.uint8, device=dev)
     vc = torch.empty(shape, dtype=torch.uint8, device=dev)
     pt = torch.from_numpy(w.page_table).to(dev)
-    ks, vs = torch.zeros(4, device=dev), torch.zeros(4, device=dev)
+    ks, vs = torch.zeros(2, device=dev), torch.zeros(2, device=dev)
+    work = torch.empty(fk.AMAX_WORK_FLOATS, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 2)]
     for e in ev:
         e[0].record()
-        fk.kv_absmax_scale(k, ks)
-        fk.kv_absmax_scale(v, vs)
+        fk.kv_absmax_scale(k, ks, work)
+        fk.kv_absmax_scale(v, vs, work)
         e[1].record()
         fk.kv_quant_append_dscale(k, v, w.ctx_seq, w.ctx_pos, pt, ks[1:2], vs[1:2], kc, vc)
         e[2].record()

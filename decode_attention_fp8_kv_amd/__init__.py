@@ -28,6 +28,7 @@ KV_FP8_E4M3 = 0
 KV_BF16 = 1
 ABORT_TAG_MISMATCH = 1
 ABORT_BAD_METADATA = 2
+AMAX_WORK_FLOATS = 512  # kv_absmax_scale's work buffer, in floats
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfp8kv.so")
@@ -77,7 +78,7 @@ def load_library() -> ctypes.CDLL:
     lib.kv_quant_append_checked.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, i32, i32, i32, i32,
                                             i32, i32, vp, vp, vp, vp]
     lib.kv_absmax_scale.restype = c.c_int
-    lib.kv_absmax_scale.argtypes = [vp, c.c_int64, vp, vp]
+    lib.kv_absmax_scale.argtypes = [vp, c.c_int64, vp, vp, vp]
     lib.kv_quant_append_dscale.restype = c.c_int
     lib.kv_quant_append_dscale.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                            vp]
@@ -264,17 +265,22 @@ def page_free(release, page_counts, page_table, free_pages, free_count, status, 
     _check("page_free", st)
 
 
-def kv_absmax_scale(x, out, stream=None):
+def kv_absmax_scale(x, out, work=None, stream=None):
     """``out[0]`` = max |x| over the finite elements of the bf16 tensor ``x``,
-    ``out[1]`` = out[0] / 448 (1 if out[0] is 0); ``out`` is a float32 [4]
-    device tensor whose last two elements are zero before the first call
-    (``torch.zeros(4)``; every call leaves them zero).  See
-    ``kv_absmax_scale`` in ``include/fp8kv.h``."""
+    ``out[1]`` = out[0] / 448 (1 if out[0] is 0); ``out`` is a float32 device
+    tensor of at least 2 elements.  ``work`` is float32 device scratch of at
+    least AMAX_WORK_FLOATS elements (any contents; one is allocated when
+    None).  See ``kv_absmax_scale`` in ``include/fp8kv.h``."""
     dev = x.device
-    if out.dtype != torch.float32 or out.numel() < 4:
-        raise ValueError("out must be a float32 tensor with 4 elements")
+    if out.dtype != torch.float32 or out.numel() < 2:
+        raise ValueError("out must be a float32 tensor with at least 2 elements")
+    if work is None:
+        work = torch.empty(AMAX_WORK_FLOATS, dtype=torch.float32, device=dev)
+    if work.dtype != torch.float32 or work.numel() < AMAX_WORK_FLOATS:
+        raise ValueError(f"work must be a float32 tensor with at least {AMAX_WORK_FLOATS} elements")
     st = load_library().kv_absmax_scale(_ptr(x, _BF16, "x", dev), x.numel(),
-                                        _ptr(out, (torch.float32,), "out", dev), _stream_handle(dev, stream))
+                                        _ptr(out, (torch.float32,), "out", dev),
+                                        _ptr(work, (torch.float32,), "work", dev), _stream_handle(dev, stream))
     _check("kv_absmax_scale", st)
 
 

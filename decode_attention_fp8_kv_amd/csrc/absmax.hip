@@ -8,11 +8,12 @@
 // largest finite magnitude onto e4m3's largest value 448 is computed on the
 // device, and kv_quant_append_dscale reads it from there, so the whole
 // hand-off needs no host round trip.  Two kernels: a grid-stride reduction
-// (four 16-byte loads in flight per thread, wave and block maxima, one
-// relaxed atomic max of the block's result into a scratch word -- for
-// non-negative floats the bit order is the value order), then one thread
-// that writes amax and scale and zeroes the scratch word for the next call
-// (the kernel boundary orders it after every block's atomic).
+// (four 16-byte loads in flight per thread, wave and block maxima, each
+// block's maximum stored to its own word of a work buffer), then one block
+// that reduces those words and writes amax and scale.  Per-block words
+// instead of one atomic max: device-scope atomics on a single address are
+// serviced one at a time, which with thousands of blocks costs more than
+// the reads themselves.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -20,14 +21,14 @@ namespace fp8kv {
 namespace {
 
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxMaxBlocks = 2048;
+constexpr int kAmaxMaxBlocks = kAmaxWorkFloats;  // one work word per block
 
 __device__ __forceinline__ float finite_abs_max(float m, uint32_t bf16_bits) {
   const float a = __builtin_fabsf(__builtin_bit_cast(float, bf16_bits << 16));
   return a <= 3.40282347e38f ? __builtin_fmaxf(m, a) : m;  // NaN and infinity fail the test
 }
 
-__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x, int64_t n, uint32_t* out) {
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x, int64_t n, float* work) {
   __shared__ float wmax[kAmaxThreads / 64];
   float m = 0.f;
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
@@ -63,29 +64,36 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x, i
     float b = wmax[0];
 #pragma unroll
     for (int k = 1; k < kAmaxThreads / 64; ++k) b = __builtin_fmaxf(b, wmax[k]);
-    // out: [0] amax, [1] scale, [2] running max (bits), [3] unused
-    __hip_atomic_fetch_max(out + 2, __builtin_bit_cast(uint32_t, b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    work[blockIdx.x] = b;
   }
 }
 
-__global__ __launch_bounds__(1) void amax_finish_kernel(uint32_t* out) {
-  const uint32_t bits = out[2];
-  const float a = __builtin_bit_cast(float, bits);
-  out[0] = bits;
-  out[1] = __builtin_bit_cast(uint32_t, a > 0.f ? a / 448.0f : 1.0f);
-  out[2] = 0u;
+__global__ __launch_bounds__(kAmaxThreads) void amax_finish_kernel(const float* work, int nb, float* out) {
+  __shared__ float wmax[kAmaxThreads / 64];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < nb; i += kAmaxThreads) m = __builtin_fmaxf(m, work[i]);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = xor_max(m, off);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = wmax[0];
+#pragma unroll
+    for (int k = 1; k < kAmaxThreads / 64; ++k) a = __builtin_fmaxf(a, wmax[k]);
+    out[0] = a;
+    out[1] = a > 0.f ? a / 448.0f : 1.0f;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_absmax_scale(const uint16_t* x, int64_t n, float* out, hipStream_t stream) {
+hipError_t launch_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, hipStream_t stream) {
   const int64_t blocks =
       std::max<int64_t>(1, std::min<int64_t>(kAmaxMaxBlocks, (n / 8 + 4 * kAmaxThreads - 1) / (4 * kAmaxThreads)));
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n,
-                     reinterpret_cast<uint32_t*>(out));
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, work);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(1), 0, stream, reinterpret_cast<uint32_t*>(out));
+  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kAmaxThreads), 0, stream, work, (int)blocks, out);
   return hipGetLastError();
 }
 

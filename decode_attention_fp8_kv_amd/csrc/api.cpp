@@ -184,11 +184,12 @@ int kv_quant_append_dscale(const uint16_t* k_new, const uint16_t* v_new, const i
                            nullptr, nullptr, nullptr, k_scale_dev, v_scale_dev, stream);
 }
 
-int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, void* stream) {
+int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, void* stream) {
+  static_assert(kAmaxWorkFloats == FP8KV_AMAX_WORK_FLOATS, "work buffer size");
   if (n < 0) return FP8KV_ERR_SHAPE;
-  if (!out || (n > 0 && !x)) return FP8KV_ERR_NULL;
-  if ((n > 0 && !aligned(x, 16)) || !aligned(out, 16)) return FP8KV_ERR_ALIGN;
-  return record_hip(launch_absmax_scale(x, n, out, static_cast<hipStream_t>(stream)));
+  if (!out || !work || (n > 0 && !x)) return FP8KV_ERR_NULL;
+  if ((n > 0 && !aligned(x, 16)) || !aligned(out, 4) || !aligned(work, 4)) return FP8KV_ERR_ALIGN;
+  return record_hip(launch_absmax_scale(x, n, out, work, static_cast<hipStream_t>(stream)));
 }
 
 int page_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, void* stream) {

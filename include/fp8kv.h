@@ -156,11 +156,12 @@ int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new,
  * kv_absmax_scale -- out[0] = max |x| over the finite elements of the BF16
  * tensor x [n] (NaNs and infinities ignored; 0 if there are none), out[1] =
  * out[0] / 448 (IEEE fp32 division), or 1 if out[0] is 0.  out is a device
- * buffer of 4 floats (16-byte aligned): out[2] is the reduction's state,
- * which must be ZERO BEFORE THE FIRST CALL (every call leaves it zero), and
- * out[3] is unused.  Calls sharing an out buffer must be ordered (same
- * stream).  x is 16-byte aligned.  Two kernels on `stream`.  Errors:
- * FP8KV_ERR_SHAPE (n < 0), FP8KV_ERR_NULL, FP8KV_ERR_ALIGN.
+ * buffer of 2 floats; work is device scratch of FP8KV_AMAX_WORK_FLOATS
+ * floats whose contents do not matter before a call and are undefined after
+ * it (no initialisation needed).  Calls sharing a work or out buffer must be
+ * ordered (same stream).  x is 16-byte aligned, out and work 4-byte
+ * aligned; all three are owned by the caller.  Two kernels on `stream`.
+ * Errors: FP8KV_ERR_SHAPE (n < 0), FP8KV_ERR_NULL, FP8KV_ERR_ALIGN.
  *
  * kv_quant_append_dscale -- kv_quant_append into an FP8 cache with the
  * scales read from device memory (e.g. out + 1 of kv_absmax_scale), so the
@@ -169,7 +170,8 @@ int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new,
  * kv_quant_append (no FP8KV_ERR_SCALE), plus FP8KV_ERR_NULL / _ALIGN for the
  * scale pointers (4-byte aligned).
  */
-int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, void* stream);
+#define FP8KV_AMAX_WORK_FLOATS 512
+int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, void* stream);
 int kv_quant_append_dscale(const uint16_t* k_new, const uint16_t* v_new,
                            const int32_t* row_seq, const int32_t* row_pos,
                            const int32_t* page_table, int32_t batch, int32_t max_pages,

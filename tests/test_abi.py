@@ -62,6 +62,7 @@ def test_python_constants_match_header():
     assert fk.KV_BF16 == _header_define("FP8KV_KV_BF16")
     assert fk.ABORT_TAG_MISMATCH == _header_define("FP8KV_ABORT_TAG_MISMATCH")
     assert fk.ABORT_BAD_METADATA == _header_define("FP8KV_ABORT_BAD_METADATA")
+    assert fk.AMAX_WORK_FLOATS == _header_define("FP8KV_AMAX_WORK_FLOATS")
 
 
 FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
@@ -180,11 +181,13 @@ def test_pool_and_checked_append_validation_codes(lib):
 
 def test_handoff_validation_codes(lib):
     E = {n: _header_define("FP8KV_ERR_" + n) for n in ["NULL", "SHAPE", "ALIGN"]}
-    assert lib.kv_absmax_scale(FAKE, -1, FAKE, None) == E["SHAPE"]
-    assert lib.kv_absmax_scale(None, 8, FAKE, None) == E["NULL"]
-    assert lib.kv_absmax_scale(FAKE, 8, None, None) == E["NULL"]
-    assert lib.kv_absmax_scale(FAKE + 2, 8, FAKE, None) == E["ALIGN"]
-    assert lib.kv_absmax_scale(FAKE, 8, FAKE + 8, None) == E["ALIGN"]
+    assert lib.kv_absmax_scale(FAKE, -1, FAKE, FAKE, None) == E["SHAPE"]
+    assert lib.kv_absmax_scale(None, 8, FAKE, FAKE, None) == E["NULL"]
+    assert lib.kv_absmax_scale(FAKE, 8, None, FAKE, None) == E["NULL"]
+    assert lib.kv_absmax_scale(FAKE, 8, FAKE, None, None) == E["NULL"]
+    assert lib.kv_absmax_scale(FAKE + 2, 8, FAKE, FAKE, None) == E["ALIGN"]
+    assert lib.kv_absmax_scale(FAKE, 8, FAKE + 2, FAKE, None) == E["ALIGN"]
+    assert lib.kv_absmax_scale(FAKE, 8, FAKE, FAKE + 2, None) == E["ALIGN"]
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8]
     tail = [FAKE, FAKE, 64, 4, 2, 64, 16, None]
     assert lib.kv_quant_append_dscale(*base, None, FAKE, *tail) == E["NULL"]
