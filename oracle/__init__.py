@@ -31,9 +31,10 @@ Modules:
 * ``oracle.page_pool``  -- generation-tagged page allocator (alloc/free) and
   the tag-checked append.
 * ``oracle.scale``      -- per-tensor amax and scale for the prefill hand-off.
+* ``oracle.int4_gemv``  -- INT4 weight-only decode GEMV (group-128 scales).
 
 Parity pins for every function live in ``tests/test_oracle_*.py``; no
 function here is "parity unpinned".
 """
 
-from . import e4m3, page_pool, paged_attn, scale  # noqa: F401
+from . import e4m3, int4_gemv, page_pool, paged_attn, scale  # noqa: F401
