@@ -21,7 +21,7 @@ __all__ = [
     "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
     "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free", "kv_absmax_scale",
-    "kv_quant_append_dscale",
+    "kv_quant_append_dscale", "int4_gemv",
 ]
 
 KV_FP8_E4M3 = 0
@@ -29,6 +29,8 @@ KV_BF16 = 1
 ABORT_TAG_MISMATCH = 1
 ABORT_BAD_METADATA = 2
 AMAX_WORK_FLOATS = 512  # kv_absmax_scale's work buffer, in floats
+INT4_GROUP = 128        # int4_gemv: weights per scale along K
+INT4_MAX_M = 64         # int4_gemv: largest number of activation rows
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfp8kv.so")
@@ -88,6 +90,8 @@ def load_library() -> ctypes.CDLL:
     lib.page_alloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.page_free.restype = c.c_int
     lib.page_free.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.int4_gemv.restype = c.c_int
+    lib.int4_gemv.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -303,3 +307,22 @@ def kv_quant_append_dscale(k_new, v_new, row_seq, row_pos, page_table, k_scale_d
         _ptr(k_cache, _CACHE[KV_FP8_E4M3], "k_cache", dev), _ptr(v_cache, _CACHE[KV_FP8_E4M3], "v_cache", dev),
         num_pages, n_rows, hkv, d, page_size, _stream_handle(dev, stream))
     _check("kv_quant_append_dscale", st)
+
+
+def int4_gemv(x, w, scales, y, stream=None):
+    """y = x @ (q * s)^T for INT4 weights: ``x`` bf16 [M][K], ``w`` int32
+    [N][K/8] words of 8 signed 4-bit codes (nibble order in
+    ``include/fp8kv.h``), ``scales`` bf16 [N][K/128], ``y`` bf16 [M][N]
+    (written).  See ``int4_gemv`` in ``include/fp8kv.h``."""
+    dev = x.device
+    if x.dim() != 2 or w.dim() != 2 or scales.dim() != 2 or y.dim() != 2:
+        raise ValueError("x, w, scales and y must be 2-D")
+    m, k = x.shape
+    n = w.shape[0]
+    if w.shape[1] * 8 != k or tuple(scales.shape) != (n, k // INT4_GROUP) or tuple(y.shape) != (m, n):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}, scales {tuple(scales.shape)}, "
+                         f"y {tuple(y.shape)}")
+    st = load_library().int4_gemv(_ptr(x, _BF16, "x", dev), _ptr(w, _I32, "w", dev),
+                                  _ptr(scales, _BF16, "scales", dev), _ptr(y, _BF16, "y", dev), m, n, k,
+                                  _stream_handle(dev, stream))
+    _check("int4_gemv", st)

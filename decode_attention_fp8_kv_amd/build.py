@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8kv.so")
 
-SOURCES = ["api.cpp", "quant_append.hip", "decode_attn.hip", "page_pool.hip", "absmax.hip"]
+SOURCES = ["api.cpp", "quant_append.hip", "decode_attn.hip", "page_pool.hip", "absmax.hip", "int4_gemv.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 HIP_FLAGS = [

@@ -238,6 +238,23 @@ int page_free(const uint8_t* release, int32_t* page_counts, const int32_t* page_
   return record_hip(launch_pool_free(p, static_cast<hipStream_t>(stream)));
 }
 
+int int4_gemv(const uint16_t* x, const uint32_t* w, const uint16_t* scales, uint16_t* y, int32_t m, int32_t n,
+              int32_t k, void* stream) {
+  if (m < 1 || m > FP8KV_INT4_MAX_M || n < 1 || k < FP8KV_INT4_GROUP || k % FP8KV_INT4_GROUP != 0)
+    return FP8KV_ERR_SHAPE;
+  if (!x || !w || !scales || !y) return FP8KV_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || !aligned(y, 2)) return FP8KV_ERR_ALIGN;
+  Int4GemvParams p{};
+  p.x = x;
+  p.w = w;
+  p.s = scales;
+  p.y = y;
+  p.m = m;
+  p.n = n;
+  p.k = k;
+  return record_hip(launch_int4_gemv(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                         int32_t page_size, int32_t max_pages, int32_t num_blocks) {
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_blocks < 0) return 0;

@@ -43,6 +43,14 @@ struct PoolParams {
   int32_t batch, max_pages, num_pages;
 };
 
+struct Int4GemvParams {
+  const uint16_t* x;                // bf16 [m][k]
+  const uint32_t* w;                // [n][k/8] words of 8 signed nibbles
+  const uint16_t* s;                // bf16 [n][k/128]
+  uint16_t* y;                      // bf16 [m][n]
+  int32_t m, n, k;
+};
+
 struct DecodeParams {
   const uint16_t* q;                // bf16 [B][Hq][D]
   const uint8_t* k_cache;           // [P][Hkv][PS][D] elements
@@ -83,6 +91,7 @@ hipError_t launch_absmax_scale(const uint16_t* x, int64_t n, float* out, float* 
 hipError_t launch_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, hipStream_t stream);
 hipError_t launch_pool_alloc(const PoolParams& p, hipStream_t stream);
 hipError_t launch_pool_free(const PoolParams& p, hipStream_t stream);
+hipError_t launch_int4_gemv(const Int4GemvParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,
                          hipStream_t stream);
 

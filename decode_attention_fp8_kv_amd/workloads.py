@@ -35,6 +35,12 @@ Recipes (every random draw comes from a ``torch.Generator`` seeded per field):
 
 The scale recipe ``amax / 448`` (448 being the largest e4m3 magnitude) is an
 input choice made by the caller of the append, not part of the append.
+
+INT4 weight-only GEMV inputs (``make_int4_gemv``): activations x ~ N(0,1)
+BF16 [M][K]; weight words uniform random 32-bit patterns (so every 4-bit
+code in [-8, 7] is equally likely); scales 2^u BF16 with u uniform in
+[-9, -5] (the range of per-group absmax/7 for weights of standard deviation
+~0.005..0.05).  No trained weights exist here: the codes are synthetic.
 """
 
 from __future__ import annotations
@@ -355,3 +361,22 @@ def make_custom(lengths, num_q_heads, num_kv_heads, head_dim, page_size, *, num_
         softmax_scale=float(np.float32(sm)), k_scale=k_scale, v_scale=v_scale, q=q,
         ctx_k=ctx_k, ctx_v=ctx_v, ctx_seq=ctx_seq, ctx_pos=ctx_pos,
         new_k=empty, new_v=empty.clone(), new_seq=none, new_pos=none.clone(), seed=seed)
+
+
+@dataclass
+class Int4GemvInputs:
+    x: torch.Tensor        # bf16 [M][K]
+    w: torch.Tensor        # int32 [N][K/8]
+    scales: torch.Tensor   # bf16 [N][K/128]
+
+
+def make_int4_gemv(m: int, n: int, k: int, seed: int = 0, device="cpu") -> Int4GemvInputs:
+    """Seeded INT4 GEMV inputs (recipe in the module docstring)."""
+    if k % 128 != 0:
+        raise ValueError("k must be a multiple of 128")
+    x = torch.randn((m, k), generator=_gen(device, seed, 101), device=device).to(torch.bfloat16)
+    w = torch.randint(-2 ** 31, 2 ** 31, (n, k // 8), generator=_gen(device, seed, 102), device=device,
+                      dtype=torch.int64).to(torch.int32)
+    u = torch.rand((n, k // 128), generator=_gen(device, seed, 103), device=device) * 4.0 - 9.0
+    scales = torch.exp2(u).to(torch.bfloat16)
+    return Int4GemvInputs(x.contiguous(), w.contiguous(), scales.contiguous())

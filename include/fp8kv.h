@@ -326,6 +326,36 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
  */
 int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads);
 
+/*
+ * INT4 weight-only decode GEMV ("ترفندهای کلادفلر برای جا دادن مدل‌های
+ * غول‌پیکر تو GPU", the second technique; "更小、更快、更安全：大规模运行Kimi和
+ * GLM", section "压缩模型权重": weights stored as 4-bit integers, which
+ * decode streams at half the bytes of FP8 and unpacks before the multiply).
+ *
+ * int4_gemv -- y[m][n] = sum_k x[m][k] * q[n][k] * s[n][k / 128], rounded
+ * once to BF16 (nearest-even) from an fp32 evaluation.
+ *
+ *   x       bf16 [m][k]            activations, 16-byte aligned
+ *   w       uint32 [n][k/8]        weights: word j of row n holds the signed
+ *                                  two's-complement 4-bit codes of k = 8j ..
+ *                                  8j+7, nibble i (bits 4i..4i+3) holding
+ *                                  k = 8j + 2i for i < 4 and k = 8j + 2(i-4)
+ *                                  + 1 for i >= 4; 16-byte aligned
+ *   scales  bf16 [n][k/128]        one scale per 128 weights of a row (no
+ *                                  zero point), 2-byte aligned
+ *   y       bf16 [m][n]            output, 2-byte aligned, must not alias
+ *                                  the inputs
+ *
+ * 1 <= m <= FP8KV_INT4_MAX_M, n >= 1, k a positive multiple of 128.  All
+ * buffers are device memory owned by the caller; one kernel on `stream`,
+ * nothing allocated, the result is deterministic.  Errors: FP8KV_ERR_SHAPE,
+ * FP8KV_ERR_NULL, FP8KV_ERR_ALIGN (nothing is launched).
+ */
+#define FP8KV_INT4_GROUP 128
+#define FP8KV_INT4_MAX_M 64
+int int4_gemv(const uint16_t* x, const uint32_t* w, const uint16_t* scales, uint16_t* y,
+              int32_t m, int32_t n, int32_t k, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -192,3 +192,19 @@ def test_handoff_validation_codes(lib):
     tail = [FAKE, FAKE, 64, 4, 2, 64, 16, None]
     assert lib.kv_quant_append_dscale(*base, None, FAKE, *tail) == E["NULL"]
     assert lib.kv_quant_append_dscale(*base, FAKE, FAKE + 2, *tail) == E["ALIGN"]
+
+
+def test_int4_gemv_validation_codes(lib):
+    E = {n: _header_define("FP8KV_ERR_" + n) for n in ["NULL", "SHAPE", "ALIGN"]}
+    assert fk.INT4_GROUP == _header_define("FP8KV_INT4_GROUP")
+    assert fk.INT4_MAX_M == _header_define("FP8KV_INT4_MAX_M")
+    ok = [FAKE, FAKE, FAKE, FAKE, 1, 64, 256, None]
+    for i, v in ((4, 0), (4, 65), (5, 0), (6, 0), (6, 64), (6, 200)):
+        a = list(ok); a[i] = v
+        assert lib.int4_gemv(*a) == E["SHAPE"], (i, v)
+    for i in range(4):
+        a = list(ok); a[i] = None
+        assert lib.int4_gemv(*a) == E["NULL"], i
+    for i, off in ((0, 8), (1, 4), (2, 1), (3, 1)):
+        a = list(ok); a[i] = FAKE + off
+        assert lib.int4_gemv(*a) == E["ALIGN"], i
