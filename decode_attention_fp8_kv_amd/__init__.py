@@ -21,7 +21,7 @@ __all__ = [
     "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
     "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free", "kv_absmax_scale",
-    "kv_quant_append_dscale", "int4_gemv",
+    "kv_quant_append_dscale", "int4_gemv", "int4_pack_weights", "int4_tile_shapes",
 ]
 
 KV_FP8_E4M3 = 0
@@ -92,6 +92,8 @@ def load_library() -> ctypes.CDLL:
     lib.page_free.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.int4_gemv.restype = c.c_int
     lib.int4_gemv.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.int4_pack_weights.restype = c.c_int
+    lib.int4_pack_weights.argtypes = [vp, vp, vp, vp, i32, i32, vp]
     _lib = lib
     return lib
 
@@ -309,20 +311,45 @@ def kv_quant_append_dscale(k_new, v_new, row_seq, row_pos, page_table, k_scale_d
     _check("kv_quant_append_dscale", st)
 
 
-def int4_gemv(x, w, scales, y, stream=None):
-    """y = x @ (q * s)^T for INT4 weights: ``x`` bf16 [M][K], ``w`` int32
-    [N][K/8] words of 8 signed 4-bit codes (nibble order in
-    ``include/fp8kv.h``), ``scales`` bf16 [N][K/128], ``y`` bf16 [M][N]
-    (written).  See ``int4_gemv`` in ``include/fp8kv.h``."""
+def int4_tile_shapes(n, k):
+    """Shapes of the tile-layout codes (int32) and scales (bf16) for an
+    [n][k] weight matrix: ((Np/16, k/128, 16, 16), (Np/16, k/128, 16))."""
+    t, g = -(-n // 16), k // INT4_GROUP
+    return (t, g, 16, 16), (t, g, 16)
+
+
+def int4_pack_weights(w_rows, s_rows, w_tiles, s_tiles, stream=None):
+    """Row layout (``w_rows`` int32 [N][K/8], ``s_rows`` bf16 [N][K/128]) ->
+    tile layout (``w_tiles`` int32, ``s_tiles`` bf16, shapes from
+    ``int4_tile_shapes``).  See ``int4_pack_weights`` in ``include/fp8kv.h``."""
+    dev = w_rows.device
+    n, kw = w_rows.shape
+    k = kw * 8
+    ws, ss = int4_tile_shapes(n, k)
+    if tuple(s_rows.shape) != (n, k // INT4_GROUP) or w_tiles.numel() != math.prod(ws) or \
+            s_tiles.numel() != math.prod(ss):
+        raise ValueError("shape mismatch between row and tile layouts")
+    st = load_library().int4_pack_weights(_ptr(w_rows, _I32, "w_rows", dev), _ptr(s_rows, _BF16, "s_rows", dev),
+                                          _ptr(w_tiles, _I32, "w_tiles", dev), _ptr(s_tiles, _BF16, "s_tiles", dev),
+                                          n, k, _stream_handle(dev, stream))
+    _check("int4_pack_weights", st)
+
+
+def int4_gemv(x, w_tiles, s_tiles, y, stream=None):
+    """y = x @ (q * s)^T for INT4 weights in the tile layout: ``x`` bf16
+    [M][K], ``w_tiles`` int32 and ``s_tiles`` bf16 with the shapes of
+    ``int4_tile_shapes(N, K)``, ``y`` bf16 [M][N] (written; N is taken from
+    it).  See ``int4_gemv`` in ``include/fp8kv.h``."""
     dev = x.device
-    if x.dim() != 2 or w.dim() != 2 or scales.dim() != 2 or y.dim() != 2:
-        raise ValueError("x, w, scales and y must be 2-D")
+    if x.dim() != 2 or y.dim() != 2:
+        raise ValueError("x and y must be 2-D")
     m, k = x.shape
-    n = w.shape[0]
-    if w.shape[1] * 8 != k or tuple(scales.shape) != (n, k // INT4_GROUP) or tuple(y.shape) != (m, n):
-        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w {tuple(w.shape)}, scales {tuple(scales.shape)}, "
-                         f"y {tuple(y.shape)}")
-    st = load_library().int4_gemv(_ptr(x, _BF16, "x", dev), _ptr(w, _I32, "w", dev),
-                                  _ptr(scales, _BF16, "scales", dev), _ptr(y, _BF16, "y", dev), m, n, k,
+    n = y.shape[1]
+    ws, ss = int4_tile_shapes(n, k)
+    if y.shape[0] != m or w_tiles.numel() != math.prod(ws) or s_tiles.numel() != math.prod(ss):
+        raise ValueError(f"shape mismatch: x {tuple(x.shape)}, w_tiles {tuple(w_tiles.shape)}, "
+                         f"s_tiles {tuple(s_tiles.shape)}, y {tuple(y.shape)}")
+    st = load_library().int4_gemv(_ptr(x, _BF16, "x", dev), _ptr(w_tiles, _I32, "w_tiles", dev),
+                                  _ptr(s_tiles, _BF16, "s_tiles", dev), _ptr(y, _BF16, "y", dev), m, n, k,
                                   _stream_handle(dev, stream))
     _check("int4_gemv", st)

@@ -238,21 +238,30 @@ int page_free(const uint8_t* release, int32_t* page_counts, const int32_t* page_
   return record_hip(launch_pool_free(p, static_cast<hipStream_t>(stream)));
 }
 
-int int4_gemv(const uint16_t* x, const uint32_t* w, const uint16_t* scales, uint16_t* y, int32_t m, int32_t n,
+int int4_gemv(const uint16_t* x, const uint32_t* w_tiles, const uint16_t* s_tiles, uint16_t* y, int32_t m, int32_t n,
               int32_t k, void* stream) {
   if (m < 1 || m > FP8KV_INT4_MAX_M || n < 1 || k < FP8KV_INT4_GROUP || k % FP8KV_INT4_GROUP != 0)
     return FP8KV_ERR_SHAPE;
-  if (!x || !w || !scales || !y) return FP8KV_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(scales, 2) || !aligned(y, 2)) return FP8KV_ERR_ALIGN;
+  if (!x || !w_tiles || !s_tiles || !y) return FP8KV_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(w_tiles, 16) || !aligned(s_tiles, 2) || !aligned(y, 2)) return FP8KV_ERR_ALIGN;
   Int4GemvParams p{};
   p.x = x;
-  p.w = w;
-  p.s = scales;
+  p.w = w_tiles;
+  p.s = s_tiles;
   p.y = y;
   p.m = m;
   p.n = n;
   p.k = k;
   return record_hip(launch_int4_gemv(p, static_cast<hipStream_t>(stream)));
+}
+
+int int4_pack_weights(const uint32_t* w_rows, const uint16_t* s_rows, uint32_t* w_tiles, uint16_t* s_tiles, int32_t n,
+                      int32_t k, void* stream) {
+  if (n < 1 || k < FP8KV_INT4_GROUP || k % FP8KV_INT4_GROUP != 0) return FP8KV_ERR_SHAPE;
+  if (!w_rows || !s_rows || !w_tiles || !s_tiles) return FP8KV_ERR_NULL;
+  if (!aligned(w_rows, 4) || !aligned(s_rows, 2) || !aligned(w_tiles, 16) || !aligned(s_tiles, 2))
+    return FP8KV_ERR_ALIGN;
+  return record_hip(launch_int4_pack(w_rows, s_rows, w_tiles, s_tiles, n, k, static_cast<hipStream_t>(stream)));
 }
 
 size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,

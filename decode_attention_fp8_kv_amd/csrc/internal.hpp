@@ -45,8 +45,8 @@ struct PoolParams {
 
 struct Int4GemvParams {
   const uint16_t* x;                // bf16 [m][k]
-  const uint32_t* w;                // [n][k/8] words of 8 signed nibbles
-  const uint16_t* s;                // bf16 [n][k/128]
+  const uint32_t* w;                // tile layout: [ceil(n/16)][k/128][16 rows][16 words]
+  const uint16_t* s;                // tile layout: bf16 [ceil(n/16)][k/128][16 rows]
   uint16_t* y;                      // bf16 [m][n]
   int32_t m, n, k;
 };
@@ -92,6 +92,8 @@ hipError_t launch_pool_init(int32_t* free_pages, int32_t* free_count, int32_t nu
 hipError_t launch_pool_alloc(const PoolParams& p, hipStream_t stream);
 hipError_t launch_pool_free(const PoolParams& p, hipStream_t stream);
 hipError_t launch_int4_gemv(const Int4GemvParams& p, hipStream_t stream);
+hipError_t launch_int4_pack(const uint32_t* w_rows, const uint16_t* s_rows, uint32_t* w_tiles, uint16_t* s_tiles,
+                            int32_t n, int32_t k, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,
                          hipStream_t stream);
 

@@ -366,17 +366,22 @@ def make_custom(lengths, num_q_heads, num_kv_heads, head_dim, page_size, *, num_
 @dataclass
 class Int4GemvInputs:
     x: torch.Tensor        # bf16 [M][K]
-    w: torch.Tensor        # int32 [N][K/8]
-    scales: torch.Tensor   # bf16 [N][K/128]
+    w: torch.Tensor        # int32 codes: tile layout [ceil(N/16)][K/128][16][16], or row layout [N][K/8]
+    scales: torch.Tensor   # bf16: tile layout [ceil(N/16)][K/128][16], or row layout [N][K/128]
+    n: int
 
 
-def make_int4_gemv(m: int, n: int, k: int, seed: int = 0, device="cpu") -> Int4GemvInputs:
-    """Seeded INT4 GEMV inputs (recipe in the module docstring)."""
+def make_int4_gemv(m: int, n: int, k: int, seed: int = 0, device="cpu", layout: str = "tiles") -> Int4GemvInputs:
+    """Seeded INT4 GEMV inputs (recipe in the module docstring).  Random
+    words are valid codes in either layout; in the tile layout the padding
+    rows hold random codes too (a GEMV must not let them reach an output)."""
     if k % 128 != 0:
         raise ValueError("k must be a multiple of 128")
+    t, g = -(-n // 16), k // 128
+    wshape, sshape = ((t, g, 16, 16), (t, g, 16)) if layout == "tiles" else ((n, k // 8), (n, g))
     x = torch.randn((m, k), generator=_gen(device, seed, 101), device=device).to(torch.bfloat16)
-    w = torch.randint(-2 ** 31, 2 ** 31, (n, k // 8), generator=_gen(device, seed, 102), device=device,
+    w = torch.randint(-2 ** 31, 2 ** 31, wshape, generator=_gen(device, seed, 102), device=device,
                       dtype=torch.int64).to(torch.int32)
-    u = torch.rand((n, k // 128), generator=_gen(device, seed, 103), device=device) * 4.0 - 9.0
+    u = torch.rand(sshape, generator=_gen(device, seed, 103), device=device) * 4.0 - 9.0
     scales = torch.exp2(u).to(torch.bfloat16)
-    return Int4GemvInputs(x.contiguous(), w.contiguous(), scales.contiguous())
+    return Int4GemvInputs(x.contiguous(), w.contiguous(), scales.contiguous(), n)

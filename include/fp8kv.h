@@ -332,19 +332,35 @@ int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads);
  * GLM", section "压缩模型权重": weights stored as 4-bit integers, which
  * decode streams at half the bytes of FP8 and unpacks before the multiply).
  *
+ * Weights use a tile layout built for the GEMV's loads; int4_pack_weights
+ * converts the common row layout into it.  Np = 16 * ceil(n / 16), G = k / 128.
+ *
+ *   row layout   codes uint32 [n][k/8]: word j of row r holds the signed
+ *                two's-complement 4-bit codes of k = 8j + i in nibble i
+ *                (bits 4i..4i+3); scales bf16 [n][G], one per 128 weights
+ *                of a row (no zero point)
+ *   tile layout  codes uint32 [Np/16][G][16][16]: tile t, group g, row
+ *                r = n - 16t, word j holds k = 128g + 8j .. +7, nibble i
+ *                holding k = 128g + 8j + 2i for i < 4 and 128g + 8j +
+ *                2(i-4) + 1 for i >= 4; scales bf16 [Np/16][G][16].  Rows
+ *                n..Np-1 are padding (int4_pack_weights writes code 0 and
+ *                scale 0 there; int4_gemv never uses them for an output row
+ *                < n).
+ *
+ * int4_pack_weights -- row layout (w_rows, s_rows) -> tile layout (w_tiles,
+ * s_tiles).  n >= 1, k a positive multiple of 128; w_rows 4-byte aligned,
+ * w_tiles 16-byte aligned, scales 2-byte aligned; outputs must not overlap
+ * the inputs.  One kernel on `stream`, bit-exact permutation of the codes.
+ * Errors: FP8KV_ERR_SHAPE, FP8KV_ERR_NULL, FP8KV_ERR_ALIGN.
+ *
  * int4_gemv -- y[m][n] = sum_k x[m][k] * q[n][k] * s[n][k / 128], rounded
  * once to BF16 (nearest-even) from an fp32 evaluation.
  *
- *   x       bf16 [m][k]            activations, 16-byte aligned
- *   w       uint32 [n][k/8]        weights: word j of row n holds the signed
- *                                  two's-complement 4-bit codes of k = 8j ..
- *                                  8j+7, nibble i (bits 4i..4i+3) holding
- *                                  k = 8j + 2i for i < 4 and k = 8j + 2(i-4)
- *                                  + 1 for i >= 4; 16-byte aligned
- *   scales  bf16 [n][k/128]        one scale per 128 weights of a row (no
- *                                  zero point), 2-byte aligned
- *   y       bf16 [m][n]            output, 2-byte aligned, must not alias
- *                                  the inputs
+ *   x        bf16 [m][k]         activations, 16-byte aligned
+ *   w_tiles  tile layout codes   16-byte aligned
+ *   s_tiles  tile layout scales  2-byte aligned
+ *   y        bf16 [m][n]         output, 2-byte aligned, must not alias the
+ *                                inputs
  *
  * 1 <= m <= FP8KV_INT4_MAX_M, n >= 1, k a positive multiple of 128.  All
  * buffers are device memory owned by the caller; one kernel on `stream`,
@@ -353,7 +369,9 @@ int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads);
  */
 #define FP8KV_INT4_GROUP 128
 #define FP8KV_INT4_MAX_M 64
-int int4_gemv(const uint16_t* x, const uint32_t* w, const uint16_t* scales, uint16_t* y,
+int int4_pack_weights(const uint32_t* w_rows, const uint16_t* s_rows, uint32_t* w_tiles,
+                      uint16_t* s_tiles, int32_t n, int32_t k, void* stream);
+int int4_gemv(const uint16_t* x, const uint32_t* w_tiles, const uint16_t* s_tiles, uint16_t* y,
               int32_t m, int32_t n, int32_t k, void* stream);
 
 #ifdef __cplusplus

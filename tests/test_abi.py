@@ -208,3 +208,17 @@ def test_int4_gemv_validation_codes(lib):
     for i, off in ((0, 8), (1, 4), (2, 1), (3, 1)):
         a = list(ok); a[i] = FAKE + off
         assert lib.int4_gemv(*a) == E["ALIGN"], i
+
+
+def test_int4_pack_validation_codes(lib):
+    E = {n: _header_define("FP8KV_ERR_" + n) for n in ["NULL", "SHAPE", "ALIGN"]}
+    ok = [FAKE, FAKE, FAKE, FAKE, 16, 256, None]
+    for i, v in ((4, 0), (5, 0), (5, 64), (5, 200)):
+        a = list(ok); a[i] = v
+        assert lib.int4_pack_weights(*a) == E["SHAPE"], (i, v)
+    for i in range(4):
+        a = list(ok); a[i] = None
+        assert lib.int4_pack_weights(*a) == E["NULL"], i
+    for i, off in ((0, 2), (1, 1), (2, 4), (3, 1)):
+        a = list(ok); a[i] = FAKE + off
+        assert lib.int4_pack_weights(*a) == E["ALIGN"], i
