@@ -20,8 +20,8 @@
 // word into four bf16 pairs in natural k order, which is what an MFMA
 // operand register holds.
 //
-// Dequantization without arithmetic: u = q + 8 (flip each nibble's top bit)
-// placed in the top four mantissa bits of 1.0 gives the bf16 value
+// Dequantization without arithmetic: u = q + 8 (each nibble's top bit
+// flipped) placed in the top four mantissa bits of 1.0 gives the bf16 value
 // 1 + u/16 = 1.5 + q/16 exactly.  The MFMA contracts x with those values,
 // and four more MFMAs with the constant -1.5 on the same x remove the
 // offset: sum_k x (1.5 + q/16) - 1.5 sum_k x = (sum_k x q) / 16.  The
@@ -49,13 +49,16 @@ constexpr int kI4LdsX = 32 * 1024;  // activations staged in LDS up to this many
 constexpr int kI4RingLds = 4;       // ring depth when the activations sit in LDS (<= 128 VGPRs)
 
 // One word of 8 weights -> 8 bf16 values 1 + (q + 8)/16 in natural k order.
+// Each pair: shift the two nibbles to bits 3..6 / 19..22, keep them, and
+// xor with 0x3FC0: that sets the exponent bits of 1.0 (0x3F80) and flips
+// the nibble's top bit, turning two's complement q into offset binary
+// q + 8.  Shift plus one three-input bit operation per pair on gfx950.
 __device__ __forceinline__ bf16x8_t i4x8_to_offset_bf16(uint32_t w) {
-  const uint32_t u = w ^ 0x88888888u;  // two's complement -> offset binary
   u32x4_t r;
-  r[0] = ((u << 3) & 0x00780078u) | 0x3F803F80u;  // nibbles 0, 4 -> k0, k1
-  r[1] = ((u >> 1) & 0x00780078u) | 0x3F803F80u;  // nibbles 1, 5 -> k2, k3
-  r[2] = ((u >> 5) & 0x00780078u) | 0x3F803F80u;  // nibbles 2, 6 -> k4, k5
-  r[3] = ((u >> 9) & 0x00780078u) | 0x3F803F80u;  // nibbles 3, 7 -> k6, k7
+  r[0] = ((w << 3) & 0x00780078u) ^ 0x3FC03FC0u;  // nibbles 0, 4 -> k0, k1
+  r[1] = ((w >> 1) & 0x00780078u) ^ 0x3FC03FC0u;  // nibbles 1, 5 -> k2, k3
+  r[2] = ((w >> 5) & 0x00780078u) ^ 0x3FC03FC0u;  // nibbles 2, 6 -> k4, k5
+  r[3] = ((w >> 9) & 0x00780078u) ^ 0x3FC03FC0u;  // nibbles 3, 7 -> k6, k7
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
