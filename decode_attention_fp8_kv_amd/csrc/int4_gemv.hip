@@ -47,6 +47,10 @@ constexpr int kI4Waves = 4;
 constexpr int kI4Threads = 64 * kI4Waves;
 constexpr int kI4LdsX = 32 * 1024;  // activations staged in LDS up to this many bytes
 constexpr int kI4RingLds = 4;       // ring depth when the activations sit in LDS (<= 128 VGPRs)
+// Activations read from registers: every 16-byte activation load feeds
+// 16 * NS weight rows, so four tiles per workgroup (the activation traffic
+// per weight byte is M / 16 of the code bytes) with a two-stage ring.
+constexpr int kI4TilesReg = 4;
 
 // One word of 8 weights -> 8 bf16 values 1 + (q + 8)/16 in natural k order.
 // Each pair: shift the two nibbles to bits 3..6 / 19..22, keep them, and
@@ -76,8 +80,10 @@ __device__ __forceinline__ void issue_stage(Stage<MB, NS, XL>& S, const u32x4_t*
                                             int g) {
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns) {
-    S.w[ns] = wrow[ns][64 * (int64_t)g];
-    S.s[ns] = srow[ns][16 * (int64_t)g];
+    // non-temporal: the codes are read once; keeping them out of the
+    // caches leaves room for the activations, which every workgroup rereads
+    S.w[ns] = __builtin_nontemporal_load(&wrow[ns][64 * (int64_t)g]);
+    S.s[ns] = __builtin_nontemporal_load(&srow[ns][16 * (int64_t)g]);
   }
   if constexpr (!XL) {
 #pragma unroll
@@ -226,9 +232,8 @@ __global__ __launch_bounds__(kI4Threads) void int4_gemv_kernel(Int4GemvParams p)
   }
 }
 
-template <int MB, int D, bool XL>
+template <int MB, int NS, int D, bool XL>
 hipError_t launch_cfg(const Int4GemvParams& p, hipStream_t stream) {
-  constexpr int NS = 2;
   const int64_t blocks = ((p.n + 15) / 16 + NS - 1) / NS;
   hipLaunchKernelGGL((int4_gemv_kernel<MB, NS, D, XL>), dim3((unsigned)blocks), dim3(kI4Threads), 0, stream, p);
   return hipGetLastError();
@@ -268,14 +273,12 @@ hipError_t launch_int4_pack(const uint32_t* w_rows, const uint16_t* s_rows, uint
 }
 
 hipError_t launch_int4_gemv(const Int4GemvParams& p, hipStream_t stream) {
-  // ring depths: as deep as keeps the kernel at <= 128 VGPRs (four waves per
-  // SIMD), except where the activations' registers leave room for two stages only
-  if (p.m <= 16 && (int64_t)p.m * p.k * 2 <= kI4LdsX) return launch_cfg<1, kI4RingLds, true>(p, stream);
+  if (p.m <= 16 && (int64_t)p.m * p.k * 2 <= kI4LdsX) return launch_cfg<1, 2, kI4RingLds, true>(p, stream);
   switch ((p.m + 15) / 16) {
-    case 1: return launch_cfg<1, 2, false>(p, stream);
-    case 2: return launch_cfg<2, 2, false>(p, stream);
-    case 3: return launch_cfg<3, 2, false>(p, stream);
-    case 4: return launch_cfg<4, 2, false>(p, stream);
+    case 1: return launch_cfg<1, kI4TilesReg, 2, false>(p, stream);
+    case 2: return launch_cfg<2, kI4TilesReg, 2, false>(p, stream);
+    case 3: return launch_cfg<3, kI4TilesReg, 2, false>(p, stream);
+    case 4: return launch_cfg<4, kI4TilesReg, 2, false>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }
