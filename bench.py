@@ -309,6 +309,60 @@ def handoff_timings(dev, reps=10):
             "total_us": round((amax_ms + app_ms) * 1e3, 1)}
 
 
+def int4_gemv_timings(dev, n=28672, k=8192, nbuf=8, reps=10, ms=(1, 16, 64)):
+    """INT4 weight-only decode GEMV y = x W^T over an n x k projection
+    (28672 x 8192: 112 MiB of 4-bit codes + 3.5 MiB of scales), M activation
+    rows.  Calls rotate over `nbuf` distinct weight sets (896 MiB, larger than
+    the Infinity Cache), so every call streams its weights from HBM.  Mean
+    over `reps` rounds after a warm-up; GB/s at the algorithmic bytes (codes
+    n*k/2 + scales n*k/64 + x 2*m*k + y 2*m*n).  The BF16 GEMV of the same
+    shape (torch.matmul, 4x the weight bytes) is timed the same way for
+    context."""
+    import torch
+    import decode_attention_fp8_kv_amd as fk
+    from decode_attention_fp8_kv_amd import workloads as W
+
+    bufs = [W.make_int4_gemv(max(ms), n, k, seed=s, device=dev) for s in range(nbuf)]
+    out = {"shape": f"{n} x {k}", "weight_sets": nbuf, "group": 128}
+    for m in ms:
+        xs = [b.x[:m].contiguous() for b in bufs]
+        ys = [torch.empty((m, n), dtype=torch.bfloat16, device=dev) for _ in range(nbuf)]
+        for i in range(2 * nbuf):
+            fk.int4_gemv(xs[i % nbuf], bufs[i % nbuf].w, bufs[i % nbuf].scales, ys[i % nbuf])
+        torch.cuda.synchronize(dev)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            for i in range(nbuf):
+                fk.int4_gemv(xs[i], bufs[i].w, bufs[i].scales, ys[i])
+        b.record()
+        torch.cuda.synchronize(dev)
+        us = a.elapsed_time(b) * 1e3 / (reps * nbuf)
+        alg = n * k // 2 + n * (k // 128) * 2 + 2 * m * k + 2 * m * n
+        out[f"m{m}"] = {"us": round(us, 2), "gbps": round(alg / (us * 1e-6) / 1e9, 1),
+                        "pct_hbm_peak": round(100.0 * alg / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 2)}
+    del bufs
+    wb = [torch.randn((n, k), device=dev, dtype=torch.bfloat16) for _ in range(2)]
+    x1 = torch.randn((1, k), device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        for wt in wb:
+            torch.matmul(x1, wt.t())
+    torch.cuda.synchronize(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        for wt in wb:
+            torch.matmul(x1, wt.t())
+    b.record()
+    torch.cuda.synchronize(dev)
+    us = a.elapsed_time(b) * 1e3 / (2 * reps)
+    out["bf16_weights_torch_m1"] = {"us": round(us, 2), "gbps": round(2 * n * k / (us * 1e-6) / 1e9, 1)}
+    out["int4_over_bf16_speed_m1"] = round(us / out["m1"]["us"], 2)
+    del wb
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(w, budget_s=15.0):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     for whole sequences taken in order, time one decode step (append of the new
@@ -583,6 +637,7 @@ def main():
         "append_checked_32_rows_us": round(res["append_checked_us"], 2),
         "page_pool": pool_timings(dev),
         "prefill_handoff": handoff_timings(dev),
+        "int4_gemv": int4_gemv_timings(dev),
         "bulk_fill": f["fill"],
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }
