@@ -25,6 +25,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,9 +41,12 @@ KERNEL_SOURCES = ["decode_attention_fp8_kv_amd/csrc/decode_attn.hip", "decode_at
                   "decode_attention_fp8_kv_amd/csrc/internal.hpp", "decode_attention_fp8_kv_amd/csrc/api.cpp"]
 
 
-def kernel_source_hash() -> str:
+INT4_SOURCES = ["decode_attention_fp8_kv_amd/csrc/int4_gemv.hip", "decode_attention_fp8_kv_amd/csrc/common.hpp"]
+
+
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -420,6 +424,9 @@ def cpu_baseline(w, budget_s=15.0):
 
 
 PROFILE_TRACE = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_trace.md")
+PROFILE_INT4 = os.path.join(ROOT, "profiles", "int4_gemv_28672x8192_counters.md")
+INT4_INSTANCES = {1: "int4_gemv_kernel<1, 2, 4, true>", 16: "int4_gemv_kernel<1, 4, 2, false>",
+                  64: "int4_gemv_kernel<4, 4, 2, false>"}
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o run -- "
              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
@@ -445,15 +452,18 @@ def summarize_profiles(out_dir: str) -> None:
 
     stats = rows(os.path.join(out_dir, "trace", "run_kernel_stats.csv"))
     keep = [r for r in stats if "fp8kv" in r["Name"]]
-    lines = ["# paged_decode_attn kernels on the conc32 workload (FP8 and BF16 KV): kernel trace", "",
+    lines = ["# Kernel trace of bench.py: paged_decode_attn on the conc32 workload (FP8 and BF16 KV), plus the "
+             "append, page pool, hand-off and INT4 GEMV legs", "",
              "Command (from the repository root; OUT is any output folder):", "",
              "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["trace"], "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     avg = {}
+    def short(kname):
+        kname = kname.replace("void ", "").replace("fp8kv::(anonymous namespace)::", "")
+        return re.sub(r"\(.*\)$", "", kname)
+
     for r in keep:
-        name = r["Name"].replace("void ", "").replace("fp8kv::(anonymous namespace)::", "")
-        name = name.replace("(fp8kv::DecodeParams)", "")
-        name = name.replace("(fp8kv::AppendParams)", "")
+        name = short(r["Name"])
         avg[name] = float(r["AverageNs"]) / 1e3
         lines.append(f"| `{name}` | {r['Calls']} | {avg[name]:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} |")
@@ -516,7 +526,37 @@ def summarize_profiles(out_dir: str) -> None:
     ]
     with open(PROFILE_COUNTERS, "w") as f:
         f.write("\n".join(out))
-    print(f"wrote {PROFILE_TRACE} and {PROFILE_COUNTERS}")
+
+    # INT4 GEMV: the instances bench.py's int4_gemv_timings runs (M = 1, 16, 64 on 28672 x 8192)
+    n_, k_ = 28672, 8192
+    fetch = defaultdict(list)
+    write = defaultdict(list)
+    for key, counter, dst in (("fetch", "FETCH_SIZE", fetch), ("write", "WRITE_SIZE", write)):
+        for r in rows(os.path.join(out_dir, f"pmc_{key}", "run_counter_collection.csv")):
+            if r["Counter_Name"] == counter and "int4_gemv_kernel" in r["Kernel_Name"]:
+                dst[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    lines = ["# INT4 weight-only GEMV on a 28672 x 8192 projection (bench.py's int4_gemv leg)", "",
+             "Commands (from the repository root; OUT is any output folder):", "",
+             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["trace"],
+             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
+             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["write"], "",
+             "Average kernel time from the trace; FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the "
+             "2 GiB device copy's factors above; algorithmic bytes = codes n*k/2 + scales n*k/64 + "
+             "x 2*m*k + y 2*m*n.", "",
+             "| M | kernel | average us | algorithmic MB | HBM MB (fetch + write) | traffic / algorithmic | "
+             "GB/s (algorithmic / average) |",
+             "|---|---|---|---|---|---|---|"]
+    for m_, kname in INT4_INSTANCES.items():
+        if kname not in avg or not fetch.get(kname) or not write.get(kname):
+            continue
+        alg4 = n_ * k_ // 2 + n_ * (k_ // 128) * 2 + 2 * m_ * k_ + 2 * m_ * n_
+        hbm = (sum(fetch[kname]) / len(fetch[kname]) * ff + sum(write[kname]) / len(write[kname]) * wf) * 1024.0
+        lines.append(f"| {m_} | `{kname}` | {avg[kname]:.2f} | {alg4 / 1e6:.1f} | {hbm / 1e6:.1f} | "
+                     f"{hbm / alg4:.3f} | {alg4 / (avg[kname] * 1e-6) / 1e9:.0f} |")
+    lines += ["", f"kernel_source_hash: {kernel_source_hash(INT4_SOURCES)} (int4_gemv.hip, common.hpp)", ""]
+    with open(PROFILE_INT4, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {PROFILE_TRACE}, {PROFILE_COUNTERS} and {PROFILE_INT4}")
 
 
 def main():
