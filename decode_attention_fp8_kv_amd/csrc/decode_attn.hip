@@ -90,21 +90,47 @@ struct Geo {
   static constexpr int CW = DC * ESZ / 4;       // words per lane per token
 };
 
+// Cache-policy operand of global_load_lds for a non-temporal load (the
+// instruction's nt bit on gfx950).
+constexpr int kCpolNonTemporal = 2;
+template <int KV>
+constexpr bool kNonTemporalK = KV == 0;  // see load_words
+
 // Load N consecutive 4-byte words with the widest aligned vector loads.
-template <int N>
+// NT: non-temporal.  The K/V stream is read once per call, and loading it
+// non-temporal (V always -- also its FP8 copy to LDS -- and K from an FP8
+// cache) streams it markedly faster: at batch 32, 68% -> 75% of 8 TB/s for
+// FP8 and 71% -> 79% for BF16.  A BF16 cache's K loads stay cached: each
+// lane's 64-byte quarter row takes four 16-byte loads, and marked
+// non-temporal they ran at 62%.
+template <int N, bool NT = false>
 __device__ __forceinline__ void load_words(const uint8_t* src, uint32_t* dst) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N; i += 4) {
-      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(src + 4 * i);
+      const u32x4_t* a = reinterpret_cast<const u32x4_t*>(src + 4 * i);
+      u32x4_t x;
+      if constexpr (NT)
+        x = __builtin_nontemporal_load(a);
+      else
+        x = *a;
       dst[i] = x[0]; dst[i + 1] = x[1]; dst[i + 2] = x[2]; dst[i + 3] = x[3];
     }
   } else if constexpr (N == 2) {
-    const u32x2_t x = *reinterpret_cast<const u32x2_t*>(src);
+    const u32x2_t* a = reinterpret_cast<const u32x2_t*>(src);
+    u32x2_t x;
+    if constexpr (NT)
+      x = __builtin_nontemporal_load(a);
+    else
+      x = *a;
     dst[0] = x[0]; dst[1] = x[1];
   } else {
     static_assert(N == 1, "unsupported word count");
-    dst[0] = *reinterpret_cast<const uint32_t*>(src);
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(src);
+    if constexpr (NT)
+      dst[0] = __builtin_nontemporal_load(a);
+    else
+      dst[0] = *a;
   }
 }
 
@@ -154,14 +180,14 @@ template <int KV, int D>
 __device__ __forceinline__ void mfma_load_k(MfmaTile<KV, D>& t, const uint8_t* kp) {
   using G_ = Geo<KV, D>;
 #pragma unroll
-  for (int bb = 0; bb < 4; ++bb) load_words<G_::KQ / 4>(kp + bb * 4 * G_::ROW, t.k[bb]);
+  for (int bb = 0; bb < 4; ++bb) load_words<G_::KQ / 4, kNonTemporalK<KV>>(kp + bb * 4 * G_::ROW, t.k[bb]);
 }
 template <int KV, int D>
 __device__ __forceinline__ void mfma_load_v(MfmaTile<KV, D>& t, const uint8_t* vp) {
   using G_ = Geo<KV, D>;
   if constexpr (KV != 0) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) load_words<G_::VW>(vp + i * G_::ROW, t.v[i]);
+    for (int i = 0; i < 16; ++i) load_words<G_::VW, true>(vp + i * G_::ROW, t.v[i]);
   }
 }
 
@@ -321,7 +347,7 @@ __device__ __forceinline__ void v_tile_to_lds(const DecodeParams& p, const PageR
     const int pid = page_of_uniform(pr, i, (m * RPI) >> 4);
     const uint8_t* src = row_ptr(p.v_cache, pid, g, p.num_kv_heads, pr.log2ps, (base_tok + t) & ps_mask, ROW) +
                          16 * (c ^ (t & (CH - 1)));
-    __builtin_amdgcn_global_load_lds(src, FP8KV_LDS(stage + m * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, FP8KV_LDS(stage + m * 1024), 16, 0, kCpolNonTemporal);
   }
 }
 
@@ -419,9 +445,9 @@ struct ValuState {
 template <int KV, int D>
 __device__ __forceinline__ void valu_load(ValuTile<KV, D>& t, const uint8_t* kp, const uint8_t* vp) {
 #pragma unroll
-  for (int u = 0; u < 8; ++u) load_words<Geo<KV, D>::CW>(kp + u * Geo<KV, D>::ROW, t.k[u]);
+  for (int u = 0; u < 8; ++u) load_words<Geo<KV, D>::CW, kNonTemporalK<KV>>(kp + u * Geo<KV, D>::ROW, t.k[u]);
 #pragma unroll
-  for (int u = 0; u < 8; ++u) load_words<Geo<KV, D>::CW>(vp + u * Geo<KV, D>::ROW, t.v[u]);
+  for (int u = 0; u < 8; ++u) load_words<Geo<KV, D>::CW, true>(vp + u * Geo<KV, D>::ROW, t.v[u]);
 }
 
 // bf16 pairs of one token's DC dims
