@@ -193,11 +193,14 @@ DEFAULT_SEEDS = {"tiny": 1, "latency": 2, "conc32": 3, "conc64": 4, "long": 5}
 
 
 def make(name: str, seed: int | None = None, device="cpu", *, bf16_subset=False,
-         inject_tags=False, batch=None, context=None) -> Workload:
+         inject_tags=False, batch=None, context=None, long_scale="p999") -> Workload:
     """Build workload ``name`` on ``device`` ("cpu" or "cuda").
 
     ``batch`` / ``context`` shrink a configuration for quick tests (same
     recipe, fewer or shorter sequences); the full sizes are the defaults.
+    ``long_scale="amax"`` gives ``long`` the amax / 448 scale instead of the
+    99.9th percentile (nothing saturates; many small values become
+    subnormal codes).
     """
     seed = DEFAULT_SEEDS[name] if seed is None else seed
     dev = torch.device(device)
@@ -278,7 +281,7 @@ def make(name: str, seed: int | None = None, device="cpu", *, bf16_subset=False,
     ctx_k, ctx_seq, ctx_pos = _rows(ctx, hkv, d, dist, seed, 10, dev, k_out)
     ctx_v, _, _ = _rows(ctx, hkv, d, dist, seed, 11, dev, v_out)
 
-    if name == "long":
+    if name == "long" and long_scale == "p999":
         k_scale = _quantile_scale(ctx_k, 0.999, seed)
         v_scale = _quantile_scale(ctx_v, 0.999, seed + 1)
     else:

@@ -103,6 +103,19 @@ def test_long_config_run_a(gpu_device):
     assert _check_config(w, FP8, gpu_device, [3]).sum() == 0
 
 
+def test_long_config_amax_scale(gpu_device):
+    # the Student-t cache quantized at amax / 448: no code saturates and a few percent are subnormal
+    w = W.make("long", device=gpu_device, long_scale="amax")
+    assert _check_config(w, FP8, gpu_device, [5]).sum() == 0
+    kc, _ = gpu_fill(w, FP8, gpu_device)            # every page of this pool is full and used
+    mag = kc.view(torch.uint8) & 0x7F
+    sub = float(((mag > 0) & (mag < 8)).float().mean())
+    sat = float((mag == 0x7E).float().mean())
+    say(f"  long amax scale: subnormal codes {100 * sub:.2f}%, saturated {100 * sat:.4f}%")
+    assert 0.01 < sub < 0.10
+    assert sat < 1e-4
+
+
 def test_long_config_run_b_injected_mismatches(gpu_device):
     w = W.make("long", device=gpu_device, inject_tags=True)
     rflags = pa.abort_flags(w.page_table, w.seq_lens, w.page_size, w.num_pages, w.page_tags, w.expected_tags)
