@@ -434,7 +434,15 @@ PROFILE_CMDS = {
              "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pmc_write -o run -- "
              "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
+    "sq": "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD "
+          "SQ_WAVES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY -f csv -d OUT/pmc_sq -o run -- "
+          "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
+    "tcc": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum -f csv -d OUT/pmc_tcc -o run -- "
+           "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
+    "lds": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS SQ_LDS_ADDR_CONFLICT SQ_LDS_IDX_ACTIVE -f csv "
+           "-d OUT/pmc_lds -o run -- python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
 }
+PROFILE_SQ = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_sq_tcc_counters.txt")
 COPY_BYTES = 2 << 30            # the device copy of copy_bandwidth(): the counters' calibration
 
 
@@ -557,6 +565,51 @@ def summarize_profiles(out_dir: str) -> None:
     with open(PROFILE_INT4, "w") as f:
         f.write("\n".join(lines))
     print(f"wrote {PROFILE_TRACE}, {PROFILE_COUNTERS} and {PROFILE_INT4}")
+    if os.path.isdir(os.path.join(out_dir, "pmc_sq")) and os.path.isdir(os.path.join(out_dir, "pmc_tcc")):
+        summarize_sq_tcc(out_dir, short)
+
+
+def summarize_sq_tcc(out_dir: str, short) -> None:
+    """Instruction mix, LDS conflicts and L2 hit rate of the FP8 decode kernel (per dispatch)."""
+    import csv
+    from collections import defaultdict
+    vals = defaultdict(lambda: defaultdict(float))
+    for sub_dir in ("pmc_sq", "pmc_tcc", "pmc_lds"):
+        if not os.path.isdir(os.path.join(out_dir, sub_dir)):
+            continue
+        with open(os.path.join(out_dir, sub_dir, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if short(r["Kernel_Name"]) == "decode_kernel<0, 128, 16, true>":
+                    vals[r["Counter_Name"]][(sub_dir, r["Dispatch_Id"])] += float(r["Counter_Value"])
+    avg = {k: sum(d.values()) / len(d) for k, d in vals.items() if d}
+    from decode_attention_fp8_kv_amd import workloads as W
+    w = W.make(WORKLOAD)
+    tiles = sum(-(-int(L) // 64) for L in w.seq_lens) * w.num_kv_heads   # (sequence, KV head, 64-token tile)
+    out = ["# decode_kernel<0, 128, 16, true> (FP8 cache) on the conc32 workload: instruction mix, LDS bank",
+           "# conflicts and L2 hits, per dispatch, from two rocprofv3 counter passes (repository root; OUT any folder):",
+           "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["sq"],
+           "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["tcc"],
+           "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["lds"],
+           "# (a counter read in two passes is averaged over both)",
+           f"kernel_source_hash: {kernel_source_hash()}",
+           f"tiles_per_dispatch: {tiles}   # (sequence, KV head, 64-token tile) triples"]
+    for k in sorted(avg):
+        out.append(f"{k}: {avg[k]:.0f}")
+    if "SQ_INSTS_MFMA" in avg:
+        out.append(f"mfma_per_tile: {avg['SQ_INSTS_MFMA'] / tiles:.2f}")
+    if "SQ_INSTS_VALU" in avg:
+        out.append(f"valu_per_tile: {avg['SQ_INSTS_VALU'] / tiles:.1f}")
+    if avg.get("SQ_INSTS_LDS"):
+        out.append(f"lds_bank_conflict_cycles_per_lds_instruction: "
+                   f"{avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_INSTS_LDS']:.3f}")
+        out.append(f"lds_bank_conflict_cycles_per_tile: {avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / tiles:.1f}   "
+                   f"# against a tile period of ~2,500 cycles per wave: not a limit")
+    if avg.get("TCC_HIT_sum", 0) + avg.get("TCC_MISS_sum", 0) > 0:
+        out.append(f"l2_hit_rate: {avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.4f}")
+    out.append("")
+    with open(PROFILE_SQ, "w") as f:
+        f.write("\n".join(out))
+    print(f"wrote {PROFILE_SQ}")
 
 
 def main():
