@@ -267,6 +267,7 @@ __global__ __launch_bounds__(256) void int4_pack_kernel(const uint32_t* wr, cons
 hipError_t launch_int4_pack(const uint32_t* w_rows, const uint16_t* s_rows, uint32_t* w_tiles, uint16_t* s_tiles,
                             int32_t n, int32_t k, hipStream_t stream) {
   const int64_t total = (int64_t)((n + 15) / 16) * (k >> 7) * 256;
+  if ((total + 255) / 256 > 0x7FFFFFFF) return hipErrorInvalidConfiguration;  // more blocks than a grid holds
   hipLaunchKernelGGL(int4_pack_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream, w_rows, s_rows,
                      w_tiles, s_tiles, n, k);
   return hipGetLastError();

@@ -178,3 +178,17 @@ def test_large_scores_and_tiny_values(gpu_device):
     w = W.make_custom([3000, 100], 64, 8, 128, 64, seed=13, dist="t3", q_scale=4.0)
     _run_case(w, FP8, gpu_device)
     _run_case(w, BF16, gpu_device)
+
+
+@pytest.mark.parametrize("kv_dtype", [FP8, BF16])
+def test_large_batch_of_short_ragged_sequences(gpu_device, kv_dtype):
+    # 700 sequences of 1..400 tokens: many more (sequence, KV head) segments than waves, so waves finish
+    # whole segments and split few; thousands of merge items; a check grid 700 sequences wide; a dozen
+    # stale pages spread over the batch
+    rng = np.random.default_rng(77)
+    lengths = rng.integers(1, 401, size=700)
+    mism = [(int(b), int(rng.integers(0, -(-int(lengths[b]) // 16)))) for b in rng.choice(700, 12, replace=False)]
+    say(f"large batch kv={kv_dtype}")
+    w = W.make_custom(lengths, 64, 8, 128, 16, seed=77, mismatch=mism)
+    out, flags, _ = _run_case(w, kv_dtype, gpu_device)
+    assert int((flags != 0).sum()) == len({b for b, _ in mism})
