@@ -30,8 +30,8 @@
 // Work decomposition
 // ------------------
 // The batch's work is the flattened list of (sequence, KV head, 64-token
-// tile) triples of the sequences that passed the check.  A 1-D grid of blocks of 4 independent waves cuts it into
-// equal contiguous shares, one per wave (see "The balanced schedule"), so
+// tile) triples of the sequences that passed the check.  A 1-D grid of
+// blocks of 4 independent waves cuts it into equal contiguous shares, one per wave (see "The balanced schedule"), so
 // every wave streams the same number of bytes whatever the length mix and
 // long sequences are split across waves (flash-decoding).  A wave keeps an
 // online-softmax state (running max m, sum l, unnormalized acc) per piece
@@ -52,10 +52,13 @@
 //     l%16 for 4 tokens) is exactly the B layout P^T needs for PV -- no data
 //     moves between lanes between the two products.
 //   * O^T = V^T P^T with v_mfma_f32_16x16x32_f16 (FP8: e4m3 -> f16 exact,
-//     P rounded to f16) or _bf16 (BF16 cache): lane l loads 16 tokens x D/16
-//     contiguous dims of V; a byte (or half-word) transpose in registers
-//     (v_perm_b32) builds the A operand.  The accumulator layout puts head
-//     l%16 in lane l, the same lane that owns its softmax state.
+//     P rounded to f16) or _bf16 (BF16 cache).  FP8: the V tile is copied
+//     global -> LDS by global_load_lds_dwordx4 and read back transposed by
+//     ds_read_b64_tr_b8.  BF16: lane l loads 16 tokens x D/16 contiguous
+//     dims of V and a half-word transpose in registers (v_perm_b32) builds
+//     the A operand.  The accumulator layout puts head l%16 in lane l, the
+//     same lane that owns its softmax state.
+//   * The K/V stream is loaded non-temporal (read once per call).
 //   * Softmax max/sum across the 4 lane groups: wave shuffles.
 // VALU family (groups of 1..4): lane = (token slot, dim chunk); dot products
 // with v_dot2_f32_bf16 and fp32 FMA, octet sums through DPP.

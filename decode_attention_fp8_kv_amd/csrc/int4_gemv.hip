@@ -16,9 +16,9 @@
 // so every wave streams sequential memory: with rows 4 KiB apart instead,
 // each DRAM page was reopened for every 64 bytes and the stream ran at half
 // the rate.  Within a word, nibble i holds k = 8j + 2i (i < 4) or
-// 8j + 2(i-4) + 1 (i >= 4): one shift and one and-or per pair then turn a
-// word into four bf16 pairs in natural k order, which is what an MFMA
-// operand register holds.
+// 8j + 2(i-4) + 1 (i >= 4): a shift and one three-input bit operation per
+// pair then turn a word into four bf16 pairs in natural k order, which is
+// what an MFMA operand register holds.
 //
 // Dequantization without arithmetic: u = q + 8 (each nibble's top bit
 // flipped) placed in the top four mantissa bits of 1.0 gives the bf16 value
@@ -47,9 +47,10 @@ constexpr int kI4Waves = 4;
 constexpr int kI4Threads = 64 * kI4Waves;
 constexpr int kI4LdsX = 32 * 1024;  // activations staged in LDS up to this many bytes
 constexpr int kI4RingLds = 4;       // ring depth when the activations sit in LDS (<= 128 VGPRs)
-// Activations read from registers: every 16-byte activation load feeds
-// 16 * NS weight rows, so four tiles per workgroup (the activation traffic
-// per weight byte is M / 16 of the code bytes) with a two-stage ring.
+// Activations read from registers: per 128-weight group a wave loads 16 * MB
+// activation rows (4 KiB per 16 rows) against NS KiB of codes, so four tiles
+// per workgroup (activation bytes ~ MB x code bytes, from L2) with a
+// two-stage ring.
 constexpr int kI4TilesReg = 4;
 
 // One word of 8 weights -> 8 bf16 values 1 + (q + 8)/16 in natural k order.
