@@ -331,8 +331,8 @@ typedef int v2i_t __attribute__((ext_vector_type(2)));
 // Physical page of 16-token group `grp16` of the round's tile `i`, for a
 // wave-uniform group (scalar read of the page list).
 __device__ __forceinline__ int page_of_uniform(const PageRound& pr, int i, int grp16) {
-  if (pr.log2ps >= 6) return __builtin_amdgcn_readlane(pr.pid, i);
-  return __builtin_amdgcn_readlane(pr.pid, (i << pr.ppt_log2) + (grp16 >> (pr.log2ps - 4)));
+  const int idx = pr.log2ps >= 6 ? i : (i << pr.ppt_log2) + (grp16 >> (pr.log2ps - 4));
+  return __builtin_amdgcn_readlane(pr.pid, idx);
 }
 
 template <int D>
@@ -641,40 +641,44 @@ __device__ __forceinline__ void run_wave(const DecodeParams& p, int b, int g, in
       // registers; then start K(i+1) into those registers; softmax + PV(i).
       // Both next-tile streams are in flight while tile i is computed, and the
       // next iteration's LDS read waits for them (the compiler waits for all
-      // LDS copies before an LDS read).  The last iteration re-reads the
-      // round's last tile so that no load sits under a condition.
+      // LDS copies before an LDS read).  The last iteration still issues both
+      // loads, so that no load sits under a condition, but computes their
+      // addresses with lane index 0 in every lane: a few cache lines of the
+      // round's last tile instead of the whole tile again.
       const float sl = p.qk_scale_log2;
       v2i_t vt[2][Geo<0, D>::NB];
       for (int i = 0; i < rt; ++i) {
         const int t0 = first_tile + (r0 + i);
         const int n1 = min(i + 1, rt - 1);
+        const int pl = lane & (i + 1 < rt ? 63 : 0);  // lane index for the prefetch addresses
         v_tile_from_lds<D>(vstage, lane, vt);
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): tile i is out of LDS before it is overwritten
         __builtin_amdgcn_sched_barrier(0);
-        v_tile_to_lds<D>(p, pr, n1, first_tile + (r0 + n1), g, lane, vstage);
+        v_tile_to_lds<D>(p, pr, n1, first_tile + (r0 + n1), g, pl, vstage);
         f32x4_t sc[4];
         mfma_qk<KV, D>(ta, st, sc);
         __builtin_amdgcn_sched_barrier(0);
-        tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + (r0 + n1), g, lane, kp, vp);
+        tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + (r0 + n1), g, pl, kp, vp);
         mfma_load_k<KV, D>(ta, kp);
         mfma_softmax_pv_lds<D>(st, sc, vt, min(L - (t0 << 6), kTileTokens), sl, lane);
       }
       __builtin_amdgcn_s_waitcnt(0);  // the last (redundant) copy has landed before LDS is reused
     } else {
     // Tile i is computed while tile i+1 loads.  The prefetch is issued on
-    // every iteration (the last one re-reads the round's last tile, which is
-    // still in cache): a prefetch under a condition would make the compiler
+    // every iteration: a prefetch under a condition would make the compiler
     // wait for it inside the current tile's math, serializing the pipeline.
+    // Past the round's last tile its addresses use lane index 0 in every
+    // lane (a few cache lines, results unused).
     const float sl = p.qk_scale_log2;
     for (int i = 0; i < rt; i += 2) {
       const int n1 = min(i + 1, rt - 1);
-      tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + (r0 + n1), g, lane, kp, vp);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, n1, first_tile + (r0 + n1), g, lane & (i + 1 < rt ? 63 : 0), kp, vp);
       load_tile<KV, D, GM, MFMA>(tb, kp, vp);
       const int t0 = first_tile + (r0 + i);
       compute_tile<KV, D, GM, MFMA>(ta, st, min(L - (t0 << 6), kTileTokens), sl, lane);
       if (i + 1 >= rt) break;
       const int n2 = min(i + 2, rt - 1);
-      tile_pointers<KV, D, GM, MFMA>(p, pr, n2, first_tile + (r0 + n2), g, lane, kp, vp);
+      tile_pointers<KV, D, GM, MFMA>(p, pr, n2, first_tile + (r0 + n2), g, lane & (i + 2 < rt ? 63 : 0), kp, vp);
       load_tile<KV, D, GM, MFMA>(ta, kp, vp);
       compute_tile<KV, D, GM, MFMA>(tb, st, min(L - ((t0 + 1) << 6), kTileTokens), sl, lane);
     }
