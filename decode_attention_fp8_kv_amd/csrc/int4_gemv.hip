@@ -48,10 +48,15 @@ constexpr int kI4Threads = 64 * kI4Waves;
 constexpr int kI4LdsX = 32 * 1024;  // activations staged in LDS up to this many bytes
 constexpr int kI4RingLds = 4;       // ring depth when the activations sit in LDS (<= 128 VGPRs)
 // Activations read from registers: per 128-weight group a wave loads 16 * MB
-// activation rows (4 KiB per 16 rows) against NS KiB of codes, so four tiles
-// per workgroup (activation bytes ~ MB x code bytes, from L2) with a
-// two-stage ring.
-constexpr int kI4TilesReg = 4;
+// activation rows (4 KiB per 16 rows) against NS KiB of codes, from L2, with
+// a two-stage ring (deeper rings measured slower).  NS is chosen per call
+// (pick_tiles): these workgroups run about one per CU, so a call takes
+// ceil(workgroups / CUs) rounds of NS tiles each; the NS with the fewest
+// tile-times wins, the larger on a tie (each activation block then feeds
+// more weight rows).  At 28,672 rows (1,792 tiles), 7 tiles per workgroup
+// make 256 workgroups and one round where 4 made 448 and two: M = 16 went
+// from 36 to 28 us and M = 64 from 84 to 60 us.
+constexpr int kI4Cus = 256;  // MI355X compute units
 
 // One word of 8 weights -> 8 bf16 values 1 + (q + 8)/16 in natural k order.
 // Each pair: shift the two nibbles to bits 3..6 / 19..22, keep them, and
@@ -274,13 +279,40 @@ hipError_t launch_int4_pack(const uint32_t* w_rows, const uint16_t* s_rows, uint
   return hipGetLastError();
 }
 
+namespace {
+
+// Tiles per workgroup on the register path (see kI4Cus).
+int pick_tiles(int64_t tiles) {
+  int best = 7;
+  int64_t best_cost = INT64_MAX;
+  for (const int ns : {7, 4, 2}) {
+    const int64_t rounds = ((tiles + ns - 1) / ns + kI4Cus - 1) / kI4Cus;
+    if (rounds * ns < best_cost) {
+      best_cost = rounds * ns;
+      best = ns;
+    }
+  }
+  return best;
+}
+
+template <int MB>
+hipError_t launch_reg(const Int4GemvParams& p, hipStream_t stream) {
+  switch (pick_tiles((p.n + 15) / 16)) {
+    case 7: return launch_cfg<MB, 7, 2, false>(p, stream);
+    case 4: return launch_cfg<MB, 4, 2, false>(p, stream);
+    default: return launch_cfg<MB, 2, 2, false>(p, stream);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_int4_gemv(const Int4GemvParams& p, hipStream_t stream) {
   if (p.m <= 16 && (int64_t)p.m * p.k * 2 <= kI4LdsX) return launch_cfg<1, 2, kI4RingLds, true>(p, stream);
   switch ((p.m + 15) / 16) {
-    case 1: return launch_cfg<1, kI4TilesReg, 2, false>(p, stream);
-    case 2: return launch_cfg<2, kI4TilesReg, 2, false>(p, stream);
-    case 3: return launch_cfg<3, kI4TilesReg, 2, false>(p, stream);
-    case 4: return launch_cfg<4, kI4TilesReg, 2, false>(p, stream);
+    case 1: return launch_reg<1>(p, stream);
+    case 2: return launch_reg<2>(p, stream);
+    case 3: return launch_reg<3>(p, stream);
+    case 4: return launch_reg<4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

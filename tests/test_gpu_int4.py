@@ -59,7 +59,9 @@ def _run(inp, dev, pad=0):
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 128), (1, 4096, 4096), (3, 1000, 2048), (16, 257, 1152),
                                    (17, 96, 384), (33, 333, 640), (48, 64, 1024), (64, 500, 2048),
-                                   (5, 31, 256), (1, 4100, 16384), (2, 48, 8192), (16, 200, 4096)])
+                                   (5, 31, 256), (1, 4100, 16384), (2, 48, 8192), (16, 200, 4096),
+                                   # 1,024 tiles: four tiles per workgroup; 1,792: seven
+                                   (16, 16384, 1024), (40, 16384, 512), (64, 28672, 256)])
 def test_int4_gemv_matches_oracle(gpu_device, m, n, k):
     say(f"int4_gemv m={m} n={n} k={k}")
     inp = W.make_int4_gemv(m, n, k, seed=m * 1000 + n)
