@@ -124,33 +124,38 @@ class Case:
         self.decode(tags=True)
 
 
-def time_steps(case, steps, warmup):
-    """Warm up, then time exactly `steps` steps between two synchronizations.
-    HIP events on the launch stream: one before the first step, then one after
-    each append and one after each decode, so the decode call is bracketed by
-    the events after its append and after itself, and the append by the
-    events after the previous decode (or the first one) and after itself.
-    Two events per step, not three: each recorded event costs the step a few
+def time_steps(case, steps, warmup, every=4):
+    """Warm up, then time exactly `steps` steps between two synchronizations
+    (the wall clock covers all of them).  Every `every`-th step is bracketed
+    by three HIP events on the launch stream -- before its append, after its
+    append, after its decode -- which give the per-call durations; the other
+    steps carry no events.  A recorded event costs the step a few
     microseconds of wall time (measured 225 / 231 / 238 us per step with 0 /
-    2 / 3 events at Conc-32) and leaves the bracketed durations unchanged."""
+    2 / 3 events on every step at Conc-32) and leaves the bracketed durations
+    unchanged, so sampling keeps that instrumentation cost out of most of
+    the timed steps."""
     torch = case.torch
     for _ in range(warmup):
         case.step()
     torch.cuda.synchronize(case.dev)
-    start = torch.cuda.Event(enable_timing=True)
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev_d = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    n_samples = (steps + every - 1) // every
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_samples)]
     t0 = time.perf_counter()
-    start.record()
     for i in range(steps):
-        case.append()
-        ev_a[i].record()
-        case.decode(tags=True)
-        ev_d[i].record()
+        if i % every == 0:
+            e0, e1, e2 = evs[i // every]
+            e0.record()
+            case.append()
+            e1.record()
+            case.decode(tags=True)
+            e2.record()
+        else:
+            case.append()
+            case.decode(tags=True)
     torch.cuda.synchronize(case.dev)
     wall = time.perf_counter() - t0
-    app_ms = np.array([start.elapsed_time(ev_a[0])] + [ev_d[i - 1].elapsed_time(ev_a[i]) for i in range(1, steps)])
-    dec_ms = np.array([ev_a[i].elapsed_time(ev_d[i]) for i in range(steps)])
+    app_ms = np.array([e0.elapsed_time(e1) for e0, e1, _ in evs])
+    dec_ms = np.array([e1.elapsed_time(e2) for _, e1, e2 in evs])
     return wall, dec_ms, app_ms
 
 
@@ -433,8 +438,8 @@ def cpu_baseline(w, budget_s=15.0):
 
 PROFILE_TRACE = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_trace.md")
 PROFILE_INT4 = os.path.join(ROOT, "profiles", "int4_gemv_28672x8192_counters.md")
-INT4_INSTANCES = {1: "int4_gemv_kernel<1, 2, 4, true>", 16: "int4_gemv_kernel<1, 4, 2, false>",
-                  64: "int4_gemv_kernel<4, 4, 2, false>"}
+INT4_INSTANCES = {1: "int4_gemv_kernel<1, 2, 4, true>", 16: "int4_gemv_kernel<1, 7, 2, false>",
+                  64: "int4_gemv_kernel<4, 7, 2, false>"}
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o run -- "
              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
@@ -471,7 +476,7 @@ def summarize_profiles(out_dir: str) -> None:
     lines = ["# Kernel trace of bench.py: paged_decode_attn on the conc32 workload (FP8 and BF16 KV), plus the "
              "append, page pool, hand-off and INT4 GEMV legs", "",
              "Command (from the repository root; OUT is any output folder):", "",
-             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["trace"], "",
+             "    export TMPDIR=/tmp && " + PROFILE_CMDS["trace"], "",
              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     avg = {}
     def short(kname):
@@ -520,8 +525,8 @@ def summarize_profiles(out_dir: str) -> None:
         "# HBM traffic of one FP8 paged_decode_attn call (check_kernel + decode_kernel<0, 128, 16, true> +",
         "# merge_kernel<128, 1>)",
         "# on the conc32 workload, from two rocprofv3 counter passes (from the repository root; OUT is any folder):",
-        "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
-        "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["write"],
+        "#   export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
+        "#   export TMPDIR=/tmp && " + PROFILE_CMDS["write"],
         "# Counters are KiB per dispatch; each is scaled by bytes / counter of the 2 GiB device copy",
         "# (__amd_rocclr_copyBuffer) that bench.py runs in the same process.",
         f"kernel_source_hash: {kernel_source_hash()}",
@@ -553,9 +558,9 @@ def summarize_profiles(out_dir: str) -> None:
                 dst[short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
     lines = ["# INT4 weight-only GEMV on a 28672 x 8192 projection (bench.py's int4_gemv leg)", "",
              "Commands (from the repository root; OUT is any output folder):", "",
-             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["trace"],
-             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
-             "    cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["write"], "",
+             "    export TMPDIR=/tmp && " + PROFILE_CMDS["trace"],
+             "    export TMPDIR=/tmp && " + PROFILE_CMDS["fetch"],
+             "    export TMPDIR=/tmp && " + PROFILE_CMDS["write"], "",
              "Average kernel time from the trace; FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the "
              "2 GiB device copy's factors above; algorithmic bytes = codes n*k/2 + scales n*k/64 + "
              "x 2*m*k + y 2*m*n.", "",
@@ -595,9 +600,9 @@ def summarize_sq_tcc(out_dir: str, short) -> None:
     tiles = sum(-(-int(L) // 64) for L in w.seq_lens) * w.num_kv_heads   # (sequence, KV head, 64-token tile)
     out = ["# decode_kernel<0, 128, 16, true> (FP8 cache) on the conc32 workload: instruction mix, LDS bank",
            "# conflicts and L2 hits, per dispatch, from two rocprofv3 counter passes (repository root; OUT any folder):",
-           "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["sq"],
-           "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["tcc"],
-           "#   cd /tmp && export TMPDIR=/tmp && " + PROFILE_CMDS["lds"],
+           "#   export TMPDIR=/tmp && " + PROFILE_CMDS["sq"],
+           "#   export TMPDIR=/tmp && " + PROFILE_CMDS["tcc"],
+           "#   export TMPDIR=/tmp && " + PROFILE_CMDS["lds"],
            "# (a counter read in two passes is averaged over both)",
            f"kernel_source_hash: {kernel_source_hash()}",
            f"tiles_per_dispatch: {tiles}   # (sequence, KV head, 64-token tile) triples"]
