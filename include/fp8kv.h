@@ -64,7 +64,7 @@ extern "C" {
 #define FP8KV_ABORT_BAD_METADATA 2u /* seq_len outside [1, max_pages*page_size], or a
                                        used page id outside [0, num_pages)            */
 
-/* Supported shapes of this build. */
+/* Supported shapes (kernels are compiled for these). */
 #define FP8KV_MAX_GROUP 16 /* num_q_heads / num_kv_heads                      */
 /* head_dim in {64, 128}; page_size a power of two in [16, 256].               */
 
