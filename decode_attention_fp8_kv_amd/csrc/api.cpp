@@ -109,7 +109,8 @@ int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_
                       const uint32_t* expected_tags, uint8_t* row_status, const float* k_scale_dev,
                       const float* v_scale_dev, void* stream) {
   if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
-  if (n_rows < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0) return FP8KV_ERR_SHAPE;
+  if (n_rows < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0 || num_kv_heads > 65535)
+    return FP8KV_ERR_SHAPE;
   if (!supported_head_dim(head_dim)) return FP8KV_ERR_UNSUPPORTED;
   const int l2ps = log2_page_size(page_size);
   if (l2ps < 0) return FP8KV_ERR_UNSUPPORTED;
@@ -307,7 +308,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
       !aligned(workspace, 256))
     return FP8KV_ERR_ALIGN;
   const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
-  // resident blocks per CU: the FP8 MFMA kernel runs 2 waves per SIMD, the others 1
+  // one resident block (4 waves) per CU by default: every decode kernel runs one wave per SIMD
   const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kBlocksPerCu);
   const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_pages, nb);
   if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;

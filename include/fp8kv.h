@@ -108,7 +108,8 @@ const char* fp8kv_last_hip_error(void);
  * outside [0, max_pages*page_size) or whose page id is outside
  * [0, num_pages) is skipped: nothing is ever written outside the pools.
  * Rows aimed at the same slot are a caller error (the winner is unspecified).
- * n_rows == 0 is valid and launches nothing.
+ * n_rows == 0 is valid and launches nothing.  num_kv_heads is at most 65535
+ * (FP8KV_ERR_SHAPE beyond).
  */
 int kv_quant_append(const uint16_t* k_new, const uint16_t* v_new,
                     const int32_t* row_seq, const int32_t* row_pos,

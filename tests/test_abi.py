@@ -128,6 +128,7 @@ def test_append_validation_codes(lib):
     assert _append(lib, pt=None) == E["NULL"]
     assert _append(lib, n_rows=-1) == E["SHAPE"]
     assert _append(lib, hkv=0) == E["SHAPE"]
+    assert _append(lib, hkv=65536) == E["SHAPE"]
     assert _append(lib, d=32) == E["UNSUPPORTED"]
     assert _append(lib, ps=48) == E["UNSUPPORTED"]
     assert _append(lib, kv_dtype=5) == E["UNSUPPORTED"]
