@@ -840,18 +840,24 @@ __device__ __forceinline__ int seq_tiles(int L, int max_tokens, uint32_t abort_b
   return (abort_bits == 0 && L >= 1 && L <= max_tokens) ? (L + kTileTokens - 1) / kTileTokens : 0;
 }
 
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
-  return v;
+// Wave scans through DPP (register-to-register lane moves, no LDS round
+// trips): row_shr:1,2,4,8 give inclusive prefix sums inside each row of 16
+// lanes, row_bcast:15 and row_bcast:31 then carry the row totals into the
+// rows above.  Lanes the pattern gives no source add the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int64_t dpp_add64(int64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)((uint64_t)v >> 32), CTRL, ROW_MASK, 0xF, false);
+  return v + (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
 }
 
-__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int64_t t = __shfl_up(v, off);
-    if (lane >= off) v += t;
-  }
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
+  v = dpp_add64<0x111, 0xF>(v);  // row_shr:1
+  v = dpp_add64<0x112, 0xF>(v);  // row_shr:2
+  v = dpp_add64<0x114, 0xF>(v);  // row_shr:4
+  v = dpp_add64<0x118, 0xF>(v);  // row_shr:8
+  v = dpp_add64<0x142, 0xA>(v);  // row_bcast:15 -> rows 1, 3
+  v = dpp_add64<0x143, 0xC>(v);  // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -1000,9 +1006,15 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
   // wave 0 writes every abort flag and marks the failed sequences' segments
   // as having nothing to merge
   int64_t mine = 0;
+  int L0 = 0, T0 = 0;  // length and tiles of sequence `lane` (the first chunk of pass 2)
   for (int b = lane; b < p.batch; b += 64) {
     const uint32_t bits = seq_abort_bits(p, b);
-    const int T = seq_tiles(p.seq_lens[b], max_tokens, bits);
+    const int Lb = p.seq_lens[b];
+    const int T = seq_tiles(Lb, max_tokens, bits);
+    if (b == lane) {
+      L0 = Lb;
+      T0 = T;
+    }
     mine += T;
     if (w == 0) {
       p.abort_flags[b] = (uint8_t)bits;
@@ -1010,7 +1022,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
         for (int g = 0; g < p.num_kv_heads; ++g) p.seg_desc[(int64_t)b * p.num_kv_heads + g] = 0;
     }
   }
-  const int64_t TT = wave_sum64(mine) * hkv;
+  const int64_t TT = readlane64(wave_inclusive_scan64(mine), 63) * hkv;
   // Never more shares than tiles: every participating wave then owns at
   // least one tile, so every wave inside a segment's span arrives.
   const int64_t nw = min((int64_t)p.num_blocks * kWavesPerBlock, TT);
@@ -1022,8 +1034,10 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
   for (int c = 0; c < p.batch; c += 64) {
     if (carry * hkv >= r1) break;
     const int b = c + lane;
-    const int T = b < p.batch ? seq_tiles(p.seq_lens[b], max_tokens, seq_abort_bits(p, b)) : 0;
-    const int64_t incl = wave_inclusive_scan64(T, lane);
+    // the first 64 sequences were read in pass 1: no second trip to memory
+    const int Lc = c == 0 ? L0 : (b < p.batch ? p.seq_lens[b] : 0);
+    const int T = c == 0 ? T0 : (b < p.batch ? seq_tiles(Lc, max_tokens, seq_abort_bits(p, b)) : 0);
+    const int64_t incl = wave_inclusive_scan64(T);
     const int64_t excl = carry + incl - T;
     const bool hit = T > 0 && excl * hkv < r1 && (excl + T) * hkv > r0;
     uint64_t mask = __ballot(hit);
@@ -1033,7 +1047,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
       const int Ti = __builtin_amdgcn_readlane(T, i);
       const int bi = c + i;
       const int64_t seq_lo = readlane64(excl, i) * hkv;
-      const int L = p.seq_lens[bi];
+      const int L = __builtin_amdgcn_readlane(Lc, i);
       const int64_t g_first = r0 > seq_lo ? (r0 - seq_lo) / Ti : 0;
       const int64_t g_last = min(hkv - 1, (r1 - 1 - seq_lo) / Ti);
       for (int64_t g = g_first; g <= g_last; ++g) {
@@ -1060,6 +1074,37 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 // WPI = 4 the waves' sums meet in LDS.  The host picks WPI = 4 when the grid
 // splits segments into many partials (small batches, long contexts).
 // ------------------------------------------------------------------------
+// Wave max / sum of a float through the same DPP scan; every lane gets the result.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int t = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, kNegInf), __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                            0xF, false);
+  return __builtin_fmaxf(v, __builtin_bit_cast(float, t));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_sum(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                                   false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max<0x111, 0xF>(v);
+  v = dpp_max<0x112, 0xF>(v);
+  v = dpp_max<0x114, 0xF>(v);
+  v = dpp_max<0x118, 0xF>(v);
+  v = dpp_max<0x142, 0xA>(v);
+  v = dpp_max<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_sum<0x111, 0xF>(v);
+  v = dpp_sum<0x112, 0xF>(v);
+  v = dpp_sum<0x114, 0xF>(v);
+  v = dpp_sum<0x118, 0xF>(v);
+  v = dpp_sum<0x142, 0xA>(v);
+  v = dpp_sum<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 constexpr int kMergeUnroll = 16;
 
 template <int D, int WPI>
@@ -1098,8 +1143,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
     }
     M = __builtin_fmaxf(M, ml[0]);
   }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) M = xor_max(M, off);
+  M = wave_max(M);
   if constexpr (WPI > 1) {
     if (lane == 0) part_m[wave] = M;
     __syncthreads();
@@ -1149,8 +1193,7 @@ __global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
       }
     }
   }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) Ls = xor_sum(Ls, off);
+  Ls = wave_sum(Ls);
   if constexpr (WPI > 1) {
 #pragma unroll
     for (int k = 0; k < DL; ++k) part_x[wave][lane * DL + k] = x[k];
