@@ -223,3 +223,25 @@ def test_int4_pack_validation_codes(lib):
     for i, off in ((0, 2), (1, 1), (2, 4), (3, 1)):
         a = list(ok); a[i] = FAKE + off
         assert lib.int4_pack_weights(*a) == E["ALIGN"], i
+
+
+def test_a_c_program_builds_and_runs_against_the_library(tmp_path):
+    """The header is plain C and the library links from C: compile
+    tests/c_abi_consumer.c with gcc against include/fp8kv.h and libfp8kv.so
+    and run it (ABI version, status strings, workspace size, argument errors;
+    nothing is launched)."""
+    import shutil
+    import subprocess
+
+    fk.load_library()
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc is not installed")
+    lib_dir = os.path.dirname(fk.lib_path)
+    exe = str(tmp_path / "c_abi_consumer")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c_abi_consumer.c"), "-o", exe, "-L", lib_dir, "-l:libfp8kv.so",
+                    f"-Wl,-rpath,{lib_dir}", "-lm"], check=True)
+    res = subprocess.run([exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    assert "passed" in res.stdout
