@@ -817,22 +817,31 @@ __device__ __forceinline__ void wave_publish(ValuState<KV, D, GM>& st, const Dec
 // All work of one call is the flattened list of (sequence b, KV head g,
 // tile t) triples, ordered b-major, then g, then t; sequence b contributes
 // num_kv_heads segments of T_b = ceil(L_b / 64) tiles (0 for a sequence
-// whose length is invalid).  Wave w of the W = min(4 * num_blocks, TT) waves
-// takes the contiguous index range [w*TT/W, (w+1)*TT/W), so every wave
-// streams the same number of tiles (+-1) whatever the length mix.  Each wave
-// derives the schedule itself from seq_lens; the host never reads device
-// memory, and waves never wait for one another.
+// whose length is invalid).  Each segment occupies delta + T_b consecutive
+// units of a flattened index: delta (0 or kPieceUnits) units that stand for
+// the cost of starting a piece of it, then one unit per tile.  Wave w of
+// the W = min(4 * num_blocks, TU) waves takes the contiguous unit range
+// [w*TU/W, (w+1)*TU/W), so every wave gets the same work (+-1 unit) --
+// tiles plus piece starts -- whatever the length mix: measured on MI355X, a
+// wave's piece start costs about one tile time, and without the charge the
+// waves that start 5-6 pieces (over several short sequences) ended last.
+// Each wave derives the schedule itself from seq_lens; the host never reads
+// device memory, and waves never wait for one another.
 //
-// A wave's range is cut into pieces, one per segment it touches.  A piece
+// A wave's range is cut into pieces, one per segment whose tiles it holds
+// (a range may end inside a segment's start charge).  A piece
 // that is a whole segment is finished in registers.  Otherwise only the
 // first and the last piece of a wave can be partial: the first is published
 // in the wave's partial slot 0 (it starts at the range start), the last in
 // slot 1.  A second kernel (one block per segment) merges the partials of
-// waves wave_of(seg_lo) .. wave_of(seg_hi - 1); the kernel boundary makes
+// waves wave_of(first tile) .. wave_of(last tile); the kernel boundary makes
 // the partials visible to it, so no wave ever synchronizes with another.
 // ------------------------------------------------------------------------
+constexpr int64_t kSeqCount = int64_t(1) << 44;  // pass 1 packs a sequence count above the tile count
+constexpr int kPieceUnits = 1;                    // schedule units a segment charges at its start
+constexpr int64_t kMinTilesForCharge = 16;        // tiles per wave from which the charge applies
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nw) { return w * total / nw; }
-// the wave whose range holds flattened index x
+// the wave whose range holds flattened unit x
 __device__ __forceinline__ int64_t wave_of(int64_t x, int64_t total, int64_t nw) { return ((x + 1) * nw - 1) / total; }
 
 // tiles of sequence b's segments, 0 if it failed the page check
@@ -1005,6 +1014,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
   // ---- pass 1: total work of the sequences that passed the page check;
   // wave 0 writes every abort flag and marks the failed sequences' segments
   // as having nothing to merge
+  // per lane: tiles (bits 0..43) + sequences with work (bits 44..) -- one scan for both
   int64_t mine = 0;
   int L0 = 0, T0 = 0;  // length and tiles of sequence `lane` (the first chunk of pass 2)
   for (int b = lane; b < p.batch; b += 64) {
@@ -1015,46 +1025,59 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
       L0 = Lb;
       T0 = T;
     }
-    mine += T;
+    mine += T + (T > 0 ? kSeqCount : 0);
     if (w == 0) {
       p.abort_flags[b] = (uint8_t)bits;
       if (T == 0)
         for (int g = 0; g < p.num_kv_heads; ++g) p.seg_desc[(int64_t)b * p.num_kv_heads + g] = 0;
     }
   }
-  const int64_t TT = readlane64(wave_inclusive_scan64(mine), 63) * hkv;
-  // Never more shares than tiles: every participating wave then owns at
-  // least one tile, so every wave inside a segment's span arrives.
-  const int64_t nw = min((int64_t)p.num_blocks * kWavesPerBlock, TT);
+  const int64_t packed = readlane64(wave_inclusive_scan64(mine), 63);
+  const int64_t TT = (packed & (kSeqCount - 1)) * hkv;  // tiles of the whole call
+  const int64_t n_segs = (packed / kSeqCount) * hkv;     // segments with work
+  // Units: every segment charges kPieceUnits at its start on top of its
+  // tiles, so a wave whose share starts pieces of several segments gets
+  // fewer tiles (a piece's start costs about one tile time).  Only when the
+  // shares are long enough for it to matter, so small calls keep one tile
+  // per unit.
+  const int64_t max_waves = (int64_t)p.num_blocks * kWavesPerBlock;
+  const int delta = TT >= kMinTilesForCharge * max_waves ? kPieceUnits : 0;
+  const int64_t TU = TT + delta * n_segs;
+  // Never more shares than units (with delta > 0 a share is >= 16 units):
+  // every wave inside a segment's span then holds some of its tiles.
+  const int64_t nw = min(max_waves, TU);
   if (w >= nw) return;
-  const int64_t r0 = range_start(w, TT, nw), r1 = range_start(w + 1, TT, nw);
+  const int64_t r0 = range_start(w, TU, nw), r1 = range_start(w + 1, TU, nw);
 
   // ---- pass 2: walk the sequences 64 at a time, process the pieces in [r0, r1)
-  int64_t carry = 0;  // tiles per KV head of all sequences before this chunk
+  int64_t carry = 0;  // units per KV head of all sequences before this chunk
   for (int c = 0; c < p.batch; c += 64) {
     if (carry * hkv >= r1) break;
     const int b = c + lane;
     // the first 64 sequences were read in pass 1: no second trip to memory
     const int Lc = c == 0 ? L0 : (b < p.batch ? p.seq_lens[b] : 0);
     const int T = c == 0 ? T0 : (b < p.batch ? seq_tiles(Lc, max_tokens, seq_abort_bits(p, b)) : 0);
-    const int64_t incl = wave_inclusive_scan64(T);
-    const int64_t excl = carry + incl - T;
-    const bool hit = T > 0 && excl * hkv < r1 && (excl + T) * hkv > r0;
+    const int U = T > 0 ? T + delta : 0;  // units per KV head of sequence b
+    const int64_t incl = wave_inclusive_scan64(U);
+    const int64_t excl = carry + incl - U;
+    const bool hit = U > 0 && excl * hkv < r1 && (excl + U) * hkv > r0;
     uint64_t mask = __ballot(hit);
     while (mask) {
       const int i = __builtin_ctzll(mask);
       mask &= mask - 1;
       const int Ti = __builtin_amdgcn_readlane(T, i);
+      const int Ui = Ti + delta;
       const int bi = c + i;
       const int64_t seq_lo = readlane64(excl, i) * hkv;
       const int L = __builtin_amdgcn_readlane(Lc, i);
-      const int64_t g_first = r0 > seq_lo ? (r0 - seq_lo) / Ti : 0;
-      const int64_t g_last = min(hkv - 1, (r1 - 1 - seq_lo) / Ti);
+      const int64_t g_first = r0 > seq_lo ? (r0 - seq_lo) / Ui : 0;
+      const int64_t g_last = min(hkv - 1, (r1 - 1 - seq_lo) / Ui);
       for (int64_t g = g_first; g <= g_last; ++g) {
-        const int64_t seg_lo = seq_lo + g * Ti;
-        const int t_lo = (int)(max(seg_lo, r0) - seg_lo);
-        const int t_hi = (int)(min(seg_lo + Ti, r1) - seg_lo);
-        wave_piece<KV, D, GM, MFMA>(p, vstage, bi, (int)g, L, Ti, t_lo, t_hi, seg_lo, r0, w, TT, nw, lane);
+        const int64_t seg_lo = seq_lo + g * Ui + delta;  // unit of the segment's first tile
+        const int64_t lo = max(seg_lo, r0), hi = min(seg_lo + Ti, r1);
+        if (lo >= hi) continue;  // this share holds only the segment's start charge
+        wave_piece<KV, D, GM, MFMA>(p, vstage, bi, (int)g, L, Ti, (int)(lo - seg_lo), (int)(hi - seg_lo), seg_lo, r0,
+                                    w, TU, nw, lane);
       }
     }
     carry += readlane64(incl, 63);
