@@ -16,6 +16,9 @@ time from HIP events on the launch stream) and the CPU oracle's rate on a
 bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py --workload latency|conc64|long --decode-only   (the other
+      configurations: the same decode legs, FP8 and BF16, without the
+      page-pool, hand-off, INT4 and CPU legs)
   python bench.py --summarize-profiles OUT   (writes profiles/ from rocprofv3 runs)
 """
 
@@ -35,7 +38,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E peak, GB/s
-WORKLOAD = "conc32"
+WORKLOAD = "conc32"             # the default workload (the headline line)
+WORKLOADS = {
+    "conc32": ("conc32: batch 32, 64 q heads / 8 KV heads, head_dim 128, page 64, context U[4096,32768] "
+               "+ 1 appended token per step, page-tag check on",
+               "synthetic (seeded; K/V/Q ~ N(0,1) bf16, 1% channels x8, random page permutation)"),
+    "latency": ("latency: batch 1, 64 q heads / 8 KV heads, head_dim 128, page 64, context 32768, "
+                "page-tag check on",
+                "synthetic (seeded; K/V/Q ~ N(0,1) bf16, random page permutation)"),
+    "conc64": ("conc64: batch 64, 64 q heads / 8 KV heads, head_dim 128, page 64, context lognormal "
+               "(median 12000, sigma 1) clipped to [512, 65536], pool exactly full, 0.1% of pages stale "
+               "(their sequences abort and are not counted); the BF16 run uses the first 32 sequences",
+               "synthetic (seeded; K/V/Q ~ N(0,1) bf16, random page permutation, stale page tags)"),
+    "long": ("long: batch 8, 64 q heads / 8 KV heads, head_dim 128, page 64, context 131072, "
+             "page-tag check on",
+             "synthetic (seeded; K/V Student-t nu=3 bf16, scale p99.9/448, Q ~ N(0,1), random page permutation)"),
+}
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_counters.txt")
 KERNEL_SOURCES = ["decode_attention_fp8_kv_amd/csrc/decode_attn.hip", "decode_attention_fp8_kv_amd/csrc/common.hpp",
                   "decode_attention_fp8_kv_amd/csrc/internal.hpp", "decode_attention_fp8_kv_amd/csrc/api.cpp"]
@@ -636,7 +654,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device-copy bandwidth measurement")
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=WORKLOAD,
+                    help="decode workload (default: the batch-32 headline)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the decode legs: no copy, page-pool, hand-off, INT4 or CPU measurements")
     args = ap.parse_args()
+    if args.decode_only:
+        args.no_copy = args.no_cpu_baseline = True
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: decode sequences shard across GPUs with no exchange "
               "between them, and no multi-GPU run is made.", file=sys.stderr)
@@ -650,16 +674,20 @@ def main():
     dev = torch.device("cuda:0")
     fk.load_library()
     copy_gbps = None if args.no_copy else copy_bandwidth(dev)
-    w = W.make(WORKLOAD, device=dev)
+    w = W.make(args.workload, device=dev)
     res = {}
     for kv, name in ((fk.KV_FP8_E4M3, "fp8"), (fk.KV_BF16, "bf16")):
         if name == "bf16" and args.no_bf16:
             continue
-        case = Case(w, kv, dev)
+        # the BF16 run of the full-pool workload takes the first 32 sequences (a BF16 cache of all 64 would
+        # not fit the pool the FP8 cache fills)
+        wk = W.make(args.workload, device=dev, bf16_subset=True) if (name == "bf16" and
+                                                                     args.workload == "conc64") else w
+        case = Case(wk, kv, dev)
         torch.cuda.synchronize(dev)
         wall, dec_ms, app_ms = time_steps(case, args.steps, args.warmup)
         flags = case.flags.cpu().numpy()
-        alg = algorithmic_bytes(w, kv, flags)
+        alg = algorithmic_bytes(wk, kv, flags)
         ok = int((flags == 0).sum())
         mean_us = float(dec_ms.mean()) * 1e3
         res[name] = {
@@ -670,13 +698,14 @@ def main():
             "decode_p95_us": float(np.percentile(dec_ms, 95)) * 1e3,
             "alg_bytes": alg,
             "gbps": alg / (mean_us * 1e-6) / 1e9,
-            "aborted": int(w.batch - ok),
+            "aborted": int(wk.batch - ok),
             "append_median_us": float(np.median(app_ms)) * 1e3,
             "fill": case.fill,
             "flushed": time_flushed(case),
         }
         if name == "fp8":
             res["tags"] = tag_overhead(case)
+        if name == "fp8" and w.new_k.shape[0] > 0:
             # the step's append, with the tag check of the page's owner
             rs = torch.empty(w.new_k.shape[0], dtype=torch.uint8, device=dev)
             nk, nv, ns, npos = case.new
@@ -700,7 +729,8 @@ def main():
                 if ":" in ln and not ln.startswith("#"):
                     key, val = ln.split(":", 1)
                     prof[key.strip()] = val.strip()
-        if prof.get("kernel_source_hash") == kernel_source_hash() and "traffic_bytes_per_launch" in prof:
+        if (args.workload == WORKLOAD and prof.get("kernel_source_hash") == kernel_source_hash()
+                and "traffic_bytes_per_launch" in prof):
             traffic = int(float(prof["traffic_bytes_per_launch"]))
     line = {
         "metric": "decode-attn tokens/s + effective KV GB/s (% HBM peak), FP8 vs BF16 KV, 1 GPU",
@@ -714,10 +744,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3",
-        "data": "synthetic (seeded; K/V/Q ~ N(0,1) bf16, 1% channels x8, random page permutation)",
+        "data": WORKLOADS[args.workload][1],
         "config": {
-            "workload": "conc32: batch 32, 64 q heads / 8 KV heads, head_dim 128, page 64, context "
-                        "U[4096,32768] + 1 appended token per step, page-tag check on",
+            "workload": WORKLOADS[args.workload][0],
             "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
             "head_dim": w.head_dim, "page_size": w.page_size, "context_tokens": int(w.seq_lens.sum()),
             "parallelism": "single GPU",
@@ -739,14 +768,16 @@ def main():
         "decode_us_flushed": {"median": f["flushed"][0], "p95": f["flushed"][1],
                               "protocol": "1 GiB read before each call (evicts the Infinity Cache), "
                                           "outside the timed region; 30 calls"},
-        "append_32_rows_us": round(f["append_median_us"], 2),
-        "append_checked_32_rows_us": round(res["append_checked_us"], 2),
-        "page_pool": pool_timings(dev),
-        "prefill_handoff": handoff_timings(dev),
-        "int4_gemv": int4_gemv_timings(dev),
         "bulk_fill": f["fill"],
         "device_copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
     }
+    if w.new_k.shape[0] > 0:
+        line["append_32_rows_us"] = round(f["append_median_us"], 2)
+        line["append_checked_32_rows_us"] = round(res["append_checked_us"], 2)
+    if not args.decode_only:
+        line["page_pool"] = pool_timings(dev)
+        line["prefill_handoff"] = handoff_timings(dev)
+        line["int4_gemv"] = int4_gemv_timings(dev)
     if "bf16" in res:
         b = res["bf16"]
         line["bf16"] = {"value": round(b["value"], 1), "unit": "tokens/s", "ms_per_step": round(b["ms_per_step"], 4),
