@@ -461,6 +461,8 @@ INT4_INSTANCES = {1: "int4_gemv_kernel<1, 2, 4, true>", 16: "int4_gemv_kernel<1,
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o run -- "
              "python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline",
+    "trace_wl": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace_{wl} -o run -- "
+                "python3 bench.py --workload {wl} --decode-only --steps 40 --warmup 5",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pmc_fetch -o run -- "
              "python3 bench.py --steps 5 --warmup 2 --no-cpu-baseline --no-bf16",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pmc_write -o run -- "
@@ -598,6 +600,42 @@ def summarize_profiles(out_dir: str) -> None:
     print(f"wrote {PROFILE_TRACE}, {PROFILE_COUNTERS} and {PROFILE_INT4}")
     if os.path.isdir(os.path.join(out_dir, "pmc_sq")) and os.path.isdir(os.path.join(out_dir, "pmc_tcc")):
         summarize_sq_tcc(out_dir, short)
+    for wl in ("latency", "conc64", "long"):
+        if os.path.isdir(os.path.join(out_dir, f"trace_{wl}")):
+            summarize_workload_trace(out_dir, wl, short)
+
+
+def summarize_workload_trace(out_dir: str, wl: str, short) -> None:
+    """Kernel times of one paged_decode_attn call (check + decode + merge) on
+    another workload, from a rocprofv3 kernel trace of bench.py --workload."""
+    import csv
+    with open(os.path.join(out_dir, f"trace_{wl}", "run_kernel_stats.csv")) as f:
+        stats = [r for r in csv.DictReader(f) if "fp8kv" in r["Name"]]
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{wl}_trace.md")
+    lines = [f"# Kernel trace of bench.py on the {wl} workload (FP8 and BF16 KV, decode legs only)", "",
+             WORKLOADS[wl][0] + ".", "",
+             "Command (from the repository root; OUT is any output folder):", "",
+             f"    export TMPDIR=/tmp && {PROFILE_CMDS['trace_wl'].format(wl=wl)}", "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    avg = {}
+    for r in stats:
+        name = short(r["Name"])
+        avg[name] = float(r["AverageNs"]) / 1e3
+        lines.append(f"| `{name}` | {r['Calls']} | {avg[name]:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} |")
+    chk = next((v for k, v in avg.items() if k.startswith("check_kernel")), None)
+    mrg = [k for k in avg if k.startswith("merge_kernel")]
+    for kv, dec in (("FP8", "decode_kernel<0, 128, 16, true>"), ("BF16", "decode_kernel<1, 128, 16, true>")):
+        if dec in avg and chk is not None and mrg:
+            m = avg[mrg[0]]
+            lines.append("")
+            lines.append(f"One {kv} call = check_kernel + `{dec}` + `{mrg[0]}` = {chk:.2f} + {avg[dec]:.2f} + "
+                         f"{m:.2f} = {chk + avg[dec] + m:.2f} us of kernel time (check and merge averaged over "
+                         f"both dtypes).")
+    lines += ["", f"kernel_source_hash: {kernel_source_hash()}", ""]
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    print(f"wrote {path}")
 
 
 def summarize_sq_tcc(out_dir: str, short) -> None:
