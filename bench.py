@@ -741,8 +741,11 @@ def main():
             "fill": case.fill,
             "flushed": time_flushed(case),
         }
-        if name == "fp8":
+        if name == "fp8" and "stale_pages" not in wk.notes:
             res["tags"] = tag_overhead(case)
+        elif name == "fp8":
+            # with stale tags, turning the check off changes the work (nothing aborts): no like-for-like
+            res["tags"] = {"skipped": "the workload has stale page tags; tags off would decode the aborted sequences"}
         if name == "fp8" and w.new_k.shape[0] > 0:
             # the step's append, with the tag check of the page's owner
             rs = torch.empty(w.new_k.shape[0], dtype=torch.uint8, device=dev)
