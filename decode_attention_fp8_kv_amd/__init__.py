@@ -21,6 +21,7 @@ __all__ = [
     "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
     "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free", "kv_absmax_scale",
+    "kv_absmax_scale_kv",
     "kv_quant_append_dscale", "int4_gemv", "int4_pack_weights", "int4_tile_shapes",
 ]
 
@@ -81,6 +82,8 @@ def load_library() -> ctypes.CDLL:
                                             i32, i32, vp, vp, vp, vp]
     lib.kv_absmax_scale.restype = c.c_int
     lib.kv_absmax_scale.argtypes = [vp, c.c_int64, vp, vp, vp]
+    lib.kv_absmax_scale_kv.restype = c.c_int
+    lib.kv_absmax_scale_kv.argtypes = [vp, vp, c.c_int64, vp, vp, vp]
     lib.kv_quant_append_dscale.restype = c.c_int
     lib.kv_quant_append_dscale.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, i32,
                                            vp]
@@ -288,6 +291,27 @@ def kv_absmax_scale(x, out, work=None, stream=None):
                                         _ptr(out, (torch.float32,), "out", dev),
                                         _ptr(work, (torch.float32,), "work", dev), _stream_handle(dev, stream))
     _check("kv_absmax_scale", st)
+
+
+def kv_absmax_scale_kv(k, v, out, work=None, stream=None):
+    """kv_absmax_scale of ``k`` and ``v`` (bf16, the same number of elements)
+    in one call: ``out[0:2]`` for k, ``out[2:4]`` for v (float32 device
+    tensor of at least 4 elements); ``work`` is float32 device scratch of at
+    least 2 * AMAX_WORK_FLOATS elements (allocated when None).  See
+    ``kv_absmax_scale_kv`` in ``include/fp8kv.h``."""
+    dev = k.device
+    if k.numel() != v.numel():
+        raise ValueError("k and v must have the same number of elements")
+    if out.dtype != torch.float32 or out.numel() < 4:
+        raise ValueError("out must be a float32 tensor with at least 4 elements")
+    if work is None:
+        work = torch.empty(2 * AMAX_WORK_FLOATS, dtype=torch.float32, device=dev)
+    if work.dtype != torch.float32 or work.numel() < 2 * AMAX_WORK_FLOATS:
+        raise ValueError(f"work must be a float32 tensor with at least {2 * AMAX_WORK_FLOATS} elements")
+    st = load_library().kv_absmax_scale_kv(_ptr(k, _BF16, "k", dev), _ptr(v, _BF16, "v", dev), k.numel(),
+                                           _ptr(out, (torch.float32,), "out", dev),
+                                           _ptr(work, (torch.float32,), "work", dev), _stream_handle(dev, stream))
+    _check("kv_absmax_scale_kv", st)
 
 
 def kv_quant_append_dscale(k_new, v_new, row_seq, row_pos, page_table, k_scale_dev, v_scale_dev, k_cache,

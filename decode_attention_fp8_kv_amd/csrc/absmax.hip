@@ -28,8 +28,13 @@ __device__ __forceinline__ float finite_abs_max(float m, uint32_t bf16_bits) {
   return a <= 3.40282347e38f ? __builtin_fmaxf(m, a) : m;  // NaN and infinity fail the test
 }
 
-__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x, int64_t n, float* work) {
+// Block y of the grid reduces tensor y (x0 or x1) into its own
+// kAmaxWorkFloats work words.
+__global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x0, const uint16_t* x1, int64_t n,
+                                                            float* work) {
   __shared__ float wmax[kAmaxThreads / 64];
+  const uint16_t* x = blockIdx.y == 0 ? x0 : x1;
+  work += (int64_t)blockIdx.y * kAmaxWorkFloats;
   float m = 0.f;
   const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
   const int64_t n8 = n >> 3;  // 16-byte words
@@ -56,8 +61,7 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x, i
   }
   for (int64_t t = 8 * n8 + (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; t < n; t += stride)
     m = finite_abs_max(m, x[t]);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) m = xor_max(m, off);
+  m = wave_max(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -68,12 +72,14 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_kernel(const uint16_t* x, i
   }
 }
 
+// Block t finishes tensor t: out[2t] = amax, out[2t + 1] = scale.
 __global__ __launch_bounds__(kAmaxThreads) void amax_finish_kernel(const float* work, int nb, float* out) {
   __shared__ float wmax[kAmaxThreads / 64];
+  work += (int64_t)blockIdx.x * kAmaxWorkFloats;
+  out += 2 * blockIdx.x;
   float m = 0.f;
   for (int i = threadIdx.x; i < nb; i += kAmaxThreads) m = __builtin_fmaxf(m, work[i]);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) m = xor_max(m, off);
+  m = wave_max(m);
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -87,13 +93,16 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_finish_kernel(const float* 
 
 }  // namespace
 
-hipError_t launch_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, hipStream_t stream) {
+hipError_t launch_absmax_scale(const uint16_t* x0, const uint16_t* x1, int tensors, int64_t n, float* out,
+                               float* work, hipStream_t stream) {
   const int64_t blocks =
       std::max<int64_t>(1, std::min<int64_t>(kAmaxMaxBlocks, (n / 8 + 4 * kAmaxThreads - 1) / (4 * kAmaxThreads)));
-  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, x, n, work);
+  hipLaunchKernelGGL(amax_kernel, dim3((unsigned)blocks, (unsigned)tensors), dim3(kAmaxThreads), 0, stream, x0, x1, n,
+                     work);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(amax_finish_kernel, dim3(1), dim3(kAmaxThreads), 0, stream, work, (int)blocks, out);
+  hipLaunchKernelGGL(amax_finish_kernel, dim3((unsigned)tensors), dim3(kAmaxThreads), 0, stream, work, (int)blocks,
+                     out);
   return hipGetLastError();
 }
 

@@ -190,7 +190,15 @@ int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, void*
   if (n < 0) return FP8KV_ERR_SHAPE;
   if (!out || !work || (n > 0 && !x)) return FP8KV_ERR_NULL;
   if ((n > 0 && !aligned(x, 16)) || !aligned(out, 4) || !aligned(work, 4)) return FP8KV_ERR_ALIGN;
-  return record_hip(launch_absmax_scale(x, n, out, work, static_cast<hipStream_t>(stream)));
+  return record_hip(launch_absmax_scale(x, x, 1, n, out, work, static_cast<hipStream_t>(stream)));
+}
+
+int kv_absmax_scale_kv(const uint16_t* k, const uint16_t* v, int64_t n, float* out, float* work, void* stream) {
+  if (n < 0) return FP8KV_ERR_SHAPE;
+  if (!out || !work || (n > 0 && (!k || !v))) return FP8KV_ERR_NULL;
+  if ((n > 0 && (!aligned(k, 16) || !aligned(v, 16))) || !aligned(out, 4) || !aligned(work, 4))
+    return FP8KV_ERR_ALIGN;
+  return record_hip(launch_absmax_scale(k, v, 2, n, out, work, static_cast<hipStream_t>(stream)));
 }
 
 int page_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, void* stream) {

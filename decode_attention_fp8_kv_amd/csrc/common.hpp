@@ -112,6 +112,42 @@ __device__ __forceinline__ float octet_sum(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Wave max / sum of a float through DPP (register-to-register lane moves,
+// no LDS round trips): row_shr:1,2,4,8 give running results inside each row
+// of 16 lanes, row_bcast:15 and row_bcast:31 carry them into the rows
+// above; lane 63 then holds the wave's result, which every lane reads.
+// Lanes the pattern gives no source combine with the identity.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int t = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -__builtin_huge_valf()), __builtin_bit_cast(int, v), CTRL, ROW_MASK,
+                                            0xF, false);
+  return __builtin_fmaxf(v, __builtin_bit_cast(float, t));
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_sum(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                                   false));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = dpp_max<0x111, 0xF>(v);
+  v = dpp_max<0x112, 0xF>(v);
+  v = dpp_max<0x114, 0xF>(v);
+  v = dpp_max<0x118, 0xF>(v);
+  v = dpp_max<0x142, 0xA>(v);
+  v = dpp_max<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = dpp_sum<0x111, 0xF>(v);
+  v = dpp_sum<0x112, 0xF>(v);
+  v = dpp_sum<0x114, 0xF>(v);
+  v = dpp_sum<0x118, 0xF>(v);
+  v = dpp_sum<0x142, 0xA>(v);
+  v = dpp_sum<0x143, 0xC>(v);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+
 // bf16 round-to-nearest-even of an fp32 value, as bits.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);

@@ -1097,37 +1097,6 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 // WPI = 4 the waves' sums meet in LDS.  The host picks WPI = 4 when the grid
 // splits segments into many partials (small batches, long contexts).
 // ------------------------------------------------------------------------
-// Wave max / sum of a float through the same DPP scan; every lane gets the result.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_max(float v) {
-  const int t = __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, kNegInf), __builtin_bit_cast(int, v), CTRL, ROW_MASK,
-                                            0xF, false);
-  return __builtin_fmaxf(v, __builtin_bit_cast(float, t));
-}
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_sum(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
-                                                                   false));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = dpp_max<0x111, 0xF>(v);
-  v = dpp_max<0x112, 0xF>(v);
-  v = dpp_max<0x114, 0xF>(v);
-  v = dpp_max<0x118, 0xF>(v);
-  v = dpp_max<0x142, 0xA>(v);
-  v = dpp_max<0x143, 0xC>(v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = dpp_sum<0x111, 0xF>(v);
-  v = dpp_sum<0x112, 0xF>(v);
-  v = dpp_sum<0x114, 0xF>(v);
-  v = dpp_sum<0x118, 0xF>(v);
-  v = dpp_sum<0x142, 0xA>(v);
-  v = dpp_sum<0x143, 0xC>(v);
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 constexpr int kMergeUnroll = 16;
 
 template <int D, int WPI>

@@ -87,7 +87,9 @@ inline int32_t check_chunks(int32_t max_pages) { return (max_pages + kCheckSlots
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream);
 constexpr int32_t kAmaxWorkFloats = 512;  // equals FP8KV_AMAX_WORK_FLOATS
-hipError_t launch_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, hipStream_t stream);
+// tensors = 1 (x0) or 2 (x0 and x1, n elements each); work holds tensors * kAmaxWorkFloats floats
+hipError_t launch_absmax_scale(const uint16_t* x0, const uint16_t* x1, int tensors, int64_t n, float* out,
+                               float* work, hipStream_t stream);
 hipError_t launch_pool_init(int32_t* free_pages, int32_t* free_count, int32_t num_pages, hipStream_t stream);
 hipError_t launch_pool_alloc(const PoolParams& p, hipStream_t stream);
 hipError_t launch_pool_free(const PoolParams& p, hipStream_t stream);

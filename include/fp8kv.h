@@ -164,6 +164,13 @@ int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new,
  * aligned; all three are owned by the caller.  Two kernels on `stream`.
  * Errors: FP8KV_ERR_SHAPE (n < 0), FP8KV_ERR_NULL, FP8KV_ERR_ALIGN.
  *
+ * kv_absmax_scale_kv -- kv_absmax_scale of a K and a V tensor of n
+ * elements each in one call: out[0], out[1] for k and out[2], out[3] for v
+ * (out is 4 floats), work is 2 * FP8KV_AMAX_WORK_FLOATS floats; each pair
+ * is bit-identical to what kv_absmax_scale gives for that tensor alone.  Two
+ * kernels on `stream` instead of four, which is what a prefill hand-off
+ * needs (both scales before the conversion).  Errors as kv_absmax_scale.
+ *
  * kv_quant_append_dscale -- kv_quant_append into an FP8 cache with the
  * scales read from device memory (e.g. out + 1 of kv_absmax_scale), so the
  * hand-off needs no host round trip.  A scale that is not finite and
@@ -173,6 +180,8 @@ int kv_quant_append_checked(const uint16_t* k_new, const uint16_t* v_new,
  */
 #define FP8KV_AMAX_WORK_FLOATS 512
 int kv_absmax_scale(const uint16_t* x, int64_t n, float* out, float* work, void* stream);
+int kv_absmax_scale_kv(const uint16_t* k, const uint16_t* v, int64_t n, float* out, float* work,
+                       void* stream);
 int kv_quant_append_dscale(const uint16_t* k_new, const uint16_t* v_new,
                            const int32_t* row_seq, const int32_t* row_pos,
                            const int32_t* page_table, int32_t batch, int32_t max_pages,

@@ -189,6 +189,10 @@ def test_handoff_validation_codes(lib):
     assert lib.kv_absmax_scale(FAKE + 2, 8, FAKE, FAKE, None) == E["ALIGN"]
     assert lib.kv_absmax_scale(FAKE, 8, FAKE + 2, FAKE, None) == E["ALIGN"]
     assert lib.kv_absmax_scale(FAKE, 8, FAKE, FAKE + 2, None) == E["ALIGN"]
+    assert lib.kv_absmax_scale_kv(FAKE, FAKE, -1, FAKE, FAKE, None) == E["SHAPE"]
+    assert lib.kv_absmax_scale_kv(FAKE, None, 8, FAKE, FAKE, None) == E["NULL"]
+    assert lib.kv_absmax_scale_kv(FAKE, FAKE, 8, FAKE, None, None) == E["NULL"]
+    assert lib.kv_absmax_scale_kv(FAKE, FAKE + 2, 8, FAKE, FAKE, None) == E["ALIGN"]
     base = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8]
     tail = [FAKE, FAKE, 64, 4, 2, 64, 16, None]
     assert lib.kv_quant_append_dscale(*base, None, FAKE, *tail) == E["NULL"]

@@ -56,6 +56,26 @@ def test_absmax_all_bf16_patterns_and_specials(gpu_device):
     assert _amax_gpu(torch.empty(0, dtype=torch.bfloat16), gpu_device).tolist() == [0.0, 1.0]
 
 
+@pytest.mark.parametrize("n", [1, 9, 4096 + 3, 33_554_432 + 5])
+def test_absmax_scale_pair_matches_single_calls_and_oracle(gpu_device, n):
+    say(f"absmax pair n={n}")
+    g = torch.Generator().manual_seed(n % 977)
+    k = (torch.randn(n, generator=g) * 3.0).to(torch.bfloat16)
+    v = (torch.randn(n, generator=g) * 0.5).to(torch.bfloat16)
+    if n > 8:
+        k[n // 3] = float("nan"); v[n // 2] = float("inf"); v[1] = -40.5
+    work = torch.full((2 * fk.AMAX_WORK_FLOATS,), 3.0e38, dtype=torch.float32, device=gpu_device)
+    out = torch.full((4,), -5.0, dtype=torch.float32, device=gpu_device)
+    fk.kv_absmax_scale_kv(k.to(gpu_device), v.to(gpu_device), out, work)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for t, (a_got, s_got) in ((k, got[0:2]), (v, got[2:4])):
+        a = sc.absmax(W.bits_u16(t))
+        assert a_got == a and s_got == sc.scale_from_amax(a)
+    assert got[0:2].tolist() == _amax_gpu(k, gpu_device).tolist()
+    assert got[2:4].tolist() == _amax_gpu(v, gpu_device).tolist()
+
+
 def test_prefill_handoff_end_to_end(gpu_device):
     # a prefill's BF16 K/V (Student-t, so saturation and subnormals occur) -> device amax and scale ->
     # device-scale append into a permuted page pool; bytes equal the oracle's append at the oracle's scale
@@ -64,9 +84,9 @@ def test_prefill_handoff_end_to_end(gpu_device):
     w = W.make_custom([L], 64, hkv, d, ps, num_pages=-(-L // ps) + 3, seed=21, dist="t3")
     k, v, pos = w.rows_of(0)
     kd, vd = k.to(gpu_device).contiguous(), v.to(gpu_device).contiguous()
-    ks, vs = torch.zeros(2, device=gpu_device), torch.zeros(2, device=gpu_device)
-    fk.kv_absmax_scale(kd, ks)
-    fk.kv_absmax_scale(vd, vs)
+    kvs = torch.zeros(4, device=gpu_device)
+    fk.kv_absmax_scale_kv(kd, vd, kvs)
+    ks, vs = kvs[0:2], kvs[2:4]
     shape = (w.num_pages, hkv, ps, d)
     kc = torch.full(shape, 0x7F, dtype=torch.uint8, device=gpu_device)
     vc = torch.full(shape, 0x7F, dtype=torch.uint8, device=gpu_device)
