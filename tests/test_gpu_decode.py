@@ -192,3 +192,40 @@ def test_large_batch_of_short_ragged_sequences(gpu_device, kv_dtype):
     w = W.make_custom(lengths, 64, 8, 128, 16, seed=77, mismatch=mism)
     out, flags, _ = _run_case(w, kv_dtype, gpu_device)
     assert int((flags != 0).sum()) == len({b for b, _ in mism})
+
+
+@pytest.mark.parametrize("num_blocks", [0, 40])
+def test_workspace_reused_with_new_data(gpu_device, num_blocks):
+    # Split segments are merged from the partials of the same call only: two
+    # inputs of one shape alternate on one workspace (and one output buffer),
+    # and every call must match the oracle for its own input -- a merge that
+    # read partials left by the previous call would not.
+    dev = gpu_device
+    lens = [2000, 4097, 3000, 65, 5000, 1, 700, 2500]
+    ws_list = [W.make_custom(lens, 64, 8, 128, 64, seed=s, mismatch=[]) for s in (101, 202)]
+    w0 = ws_list[0]
+    ws = fk.alloc_workspace(w0.batch, w0.num_q_heads, w0.num_kv_heads, w0.head_dim, w0.page_size,
+                            w0.page_table.shape[1], num_blocks, device=dev)
+    ws.fill_(0xA5)
+    out = torch.empty(tuple(w0.q.shape), dtype=torch.bfloat16, device=dev)
+    flags = torch.empty((w0.batch,), dtype=torch.uint8, device=dev)
+    prepared = []
+    for w in ws_list:
+        kc, vc = gpu_fill(w, FP8, dev)
+        okc, ovc = oracle_fill(w, FP8)
+        ref, rflags = oracle_decode(w, FP8, okc, ovc, tags_on=True)
+        prepared.append((w, kc, vc, ref, rflags, torch.from_numpy(w.page_table).to(dev),
+                         torch.from_numpy(np.asarray(w.seq_lens, np.int32)).to(dev),
+                         torch.from_numpy(w.page_tags.view(np.int32)).to(dev),
+                         torch.from_numpy(np.ascontiguousarray(w.expected_tags).view(np.int32)).to(dev),
+                         w.q.to(dev).contiguous()))
+    for i in range(6):
+        w, kc, vc, ref, rflags, pt, sl, tags, exp, q = prepared[i % 2]
+        say(f"reused workspace call {i} num_blocks={num_blocks}")
+        fk.paged_decode_attn(q, kc, vc, pt, sl, out, flags, ws, kv_dtype=FP8, k_scale=w.k_scale,
+                             v_scale=w.v_scale, page_tags=tags, expected_tags=exp,
+                             softmax_scale=w.softmax_scale, num_blocks=num_blocks)
+        torch.cuda.synchronize(dev)
+        got_flags = flags.cpu().numpy()
+        assert np.array_equal(got_flags, rflags)
+        compare_outputs(W.bits_u16(out), ref, got_flags)
