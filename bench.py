@@ -466,7 +466,7 @@ def cpu_baseline(w, budget_s=15.0):
 
 PROFILE_TRACE = os.path.join(ROOT, "profiles", "decode_kernel_conc32_fp8_trace.md")
 PROFILE_INT4 = os.path.join(ROOT, "profiles", "int4_gemv_28672x8192_counters.md")
-INT4_INSTANCES = {1: "int4_gemv_kernel<1, 2, 4, true>", 16: "int4_gemv_kernel<1, 7, 2, false>",
+INT4_INSTANCES = {1: "int4_gemv_kernel<1, 7, 2, true>", 16: "int4_gemv_kernel<1, 7, 2, false>",
                   64: "int4_gemv_kernel<4, 7, 2, false>"}
 PROFILE_CMDS = {
     "trace": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace -o run -- "

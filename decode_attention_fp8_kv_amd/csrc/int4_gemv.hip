@@ -307,7 +307,14 @@ hipError_t launch_reg(const Int4GemvParams& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_int4_gemv(const Int4GemvParams& p, hipStream_t stream) {
-  if (p.m <= 16 && (int64_t)p.m * p.k * 2 <= kI4LdsX) return launch_cfg<1, 2, kI4RingLds, true>(p, stream);
+  if (p.m <= 16 && (int64_t)p.m * p.k * 2 <= kI4LdsX) {
+    // Activations in LDS.  When 7 tiles per workgroup take the fewest
+    // tile-times, one workgroup per CU with a two-stage ring (at 28,672
+    // rows: 24.6 us vs 25.9 us with 2 tiles per workgroup, four workgroups
+    // per CU and a four-stage ring).
+    if (pick_tiles((p.n + 15) / 16) == 7) return launch_cfg<1, 7, 2, true>(p, stream);
+    return launch_cfg<1, 2, kI4RingLds, true>(p, stream);
+  }
   switch ((p.m + 15) / 16) {
     case 1: return launch_reg<1>(p, stream);
     case 2: return launch_reg<2>(p, stream);

@@ -61,7 +61,9 @@ def _run(inp, dev, pad=0):
                                    (17, 96, 384), (33, 333, 640), (48, 64, 1024), (64, 500, 2048),
                                    (5, 31, 256), (1, 4100, 16384), (2, 48, 8192), (16, 200, 4096),
                                    # 1,024 tiles: four tiles per workgroup; 1,792: seven
-                                   (16, 16384, 1024), (40, 16384, 512), (64, 28672, 256)])
+                                   (16, 16384, 1024), (40, 16384, 512), (64, 28672, 256),
+                                   # activations in LDS, seven tiles per workgroup (the last one ragged)
+                                   (1, 28672, 1024), (3, 28600, 512)])
 def test_int4_gemv_matches_oracle(gpu_device, m, n, k):
     say(f"int4_gemv m={m} n={n} k={k}")
     inp = W.make_int4_gemv(m, n, k, seed=m * 1000 + n)
