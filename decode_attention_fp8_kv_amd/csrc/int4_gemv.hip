@@ -102,6 +102,36 @@ __device__ __forceinline__ void issue_stage(Stage<MB, NS, XL>& S, const u32x4_t*
 template <int MB, int NS, bool XL>
 __device__ __forceinline__ void compute_stage(const Stage<MB, NS, XL>& S, f32x4_t (&acc)[NS][MB], bf16x8_t neg15,
                                               const bf16x8_t* xl, int g) {
+  if constexpr (MB > 1) {
+    // Tiles outside, activation blocks inside: one tile's unpacked codes are
+    // live at a time instead of all NS (at MB = 4, NS = 7 this keeps the
+    // kernel within its registers; 58 us vs 60.5 us at 64 x 28,672 x 8,192).
+    // Every output sees the same operations in the same order either way.
+    f32x4_t corr[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      corr[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        corr[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.a[mb][i], neg15, corr[mb], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ns = 0; ns < NS; ++ns) {
+      bf16x8_t b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) b[i] = i4x8_to_offset_bf16(S.w[ns][i]);
+      const float sc = 16.f * bf16_bits_to_f32(S.s[ns]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        f32x4_t t = corr[mb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(S.a[mb][i], b[i], t, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[ns][mb][v] += sc * t[v];
+      }
+    }
+    return;
+  }
   bf16x8_t b[NS][4];
 #pragma unroll
   for (int ns = 0; ns < NS; ++ns)
