@@ -229,3 +229,68 @@ def test_workspace_reused_with_new_data(gpu_device, num_blocks):
         got_flags = flags.cpu().numpy()
         assert np.array_equal(got_flags, rflags)
         compare_outputs(W.bits_u16(out), ref, got_flags)
+
+
+def test_concurrent_calls_from_two_threads_on_two_streams(gpu_device):
+    # Two host threads, each with its own stream, workspace, inputs and
+    # outputs, call the library at the same time (ctypes releases the GIL
+    # during a call); every result equals the same call made alone.
+    import threading
+
+    dev = gpu_device
+    cases = []
+    for seed, lens in ((31, [2000, 5000, 64]), (32, [4097, 1, 900, 3000])):
+        w = W.make_custom(lens, 64, 8, 128, 64, seed=seed, mismatch=[(0, 1)])
+        kc, vc = gpu_fill(w, FP8, dev)
+        cases.append(dict(
+            w=w, kc=kc, vc=vc, q=w.q.to(dev).contiguous(), pt=torch.from_numpy(w.page_table).to(dev),
+            sl=torch.from_numpy(w.seq_lens.astype(np.int32)).to(dev),
+            tags=torch.from_numpy(w.page_tags.view(np.int32)).to(dev),
+            exp=torch.from_numpy(np.ascontiguousarray(w.expected_tags).view(np.int32)).to(dev),
+            ws=fk.alloc_workspace(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                                  w.page_table.shape[1], device=dev),
+            out=torch.full(tuple(w.q.shape), 0, dtype=torch.bfloat16, device=dev),
+            flags=torch.zeros((w.batch,), dtype=torch.uint8, device=dev)))
+
+    def call(c):
+        w = c["w"]
+        fk.paged_decode_attn(c["q"], c["kc"], c["vc"], c["pt"], c["sl"], c["out"], c["flags"], c["ws"],
+                             kv_dtype=FP8, k_scale=w.k_scale, v_scale=w.v_scale, page_tags=c["tags"],
+                             expected_tags=c["exp"], softmax_scale=w.softmax_scale)
+
+    refs = []
+    for c in cases:
+        call(c)
+        torch.cuda.synchronize(dev)
+        refs.append((c["out"].clone(), c["flags"].clone()))
+        c["out"].view(torch.int16).fill_(OUT_SENTINEL)
+    assert refs[0][1].tolist()[0] == fk.ABORT_TAG_MISMATCH  # sequence 0 aborts: its rows stay untouched
+    torch.cuda.synchronize(dev)
+
+    errors = []
+
+    def worker(c):
+        try:
+            s = torch.cuda.Stream(dev)
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    call(c)
+            s.synchronize()
+        except Exception as e:  # surfaced in the main thread
+            errors.append(e)
+
+    say("two threads, two streams")
+    threads = [threading.Thread(target=worker, args=(c,)) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    assert not any(t.is_alive() for t in threads)
+    torch.cuda.synchronize(dev)
+    for c, (ro, rf) in zip(cases, refs):
+        assert torch.equal(c["flags"], rf)
+        b_ok = rf.cpu().numpy() == 0
+        got, want = c["out"].view(torch.int16).cpu().numpy(), ro.view(torch.int16).cpu().numpy()
+        assert np.array_equal(got[b_ok], want[b_ok])
+        assert np.all(got[~b_ok] == OUT_SENTINEL)
