@@ -1086,7 +1086,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 
 // ------------------------------------------------------------------------
 // The merge kernel: one item per (sequence, KV head, query head of the
-// group), handled by WPI waves (1 or 4; 4 / WPI items per block).  Segments
+// group), handled by WPI waves (1: four items per block; kWideMergeWaves:
+// one item per block).  Segments
 // finished inside one wave were written by the decode kernel, and aborted
 // sequences have no descriptor; the others' partials are combined by
 // log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M),
@@ -1094,21 +1095,27 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 // waves split its partials; lanes hold the statistics of up to 64 partials
 // at a time and the head's output dims; each partial's accumulator row is
 // one coalesced load per wave, kMergeUnroll of them in flight per lane; with
-// WPI = 4 the waves' sums meet in LDS.  The host picks WPI = 4 when the grid
-// splits segments into many partials (small batches, long contexts).
+// WPI > 1 the waves' sums meet in LDS.  The host picks the wide form when
+// the grid splits segments into many partials (small batches, long
+// contexts).
 // ------------------------------------------------------------------------
 constexpr int kMergeUnroll = 16;
+// Waves per query head when segments have many partials: at one 32k-token
+// sequence (128 partials per segment) 8 waves of 16 partials each took
+// 27.0 us per call, 4 waves of 32 27.6 us, 16 waves of 8 28.3 us.
+constexpr int kWideMergeWaves = 8;
 
 template <int D, int WPI>
-__global__ __launch_bounds__(kBlockThreads) void merge_kernel(DecodeParams p) {
-  constexpr int DL = D / 64;  // output dims per lane
-  __shared__ float part_x[kWavesPerBlock][D];
-  __shared__ float part_l[kWavesPerBlock];
-  __shared__ float part_m[kWavesPerBlock];
+__global__ __launch_bounds__(64 * (WPI > kWavesPerBlock ? WPI : kWavesPerBlock)) void merge_kernel(DecodeParams p) {
+  constexpr int DL = D / 64;                                        // output dims per lane
+  constexpr int WPB = WPI > kWavesPerBlock ? WPI : kWavesPerBlock;  // waves per block
+  __shared__ float part_x[WPB][D];
+  __shared__ float part_l[WPB];
+  __shared__ float part_m[WPB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = wave % WPI, w0 = wave - sub;  // this wave's share of the item; the item's first wave
   const int G = p.group;
-  const int64_t item = (int64_t)blockIdx.x * (kWavesPerBlock / WPI) + wave / WPI;
+  const int64_t item = (int64_t)blockIdx.x * (WPB / WPI) + wave / WPI;
   if (item >= (int64_t)p.batch * p.num_q_heads) return;  // uniform over the item's waves
   const int64_t seg = item / G;
   const int h = (int)(item - seg * G);
@@ -1224,10 +1231,12 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int64_t merge_items = (int64_t)p.batch * p.num_q_heads;  // one per query head
   // Segments split into many partials (more waves than 16 per segment when
-  // every segment is as long as the page table allows) get 4 waves each.
+  // every segment is as long as the page table allows) get kWideMergeWaves
+  // waves per query head.
   const bool wide = (int64_t)p.num_blocks * kWavesPerBlock > 16 * (int64_t)p.batch * p.num_kv_heads;
   if (wide) {
-    hipLaunchKernelGGL((merge_kernel<D, 4>), dim3((unsigned)merge_items), dim3(kBlockThreads), 0, stream, p);
+    hipLaunchKernelGGL((merge_kernel<D, kWideMergeWaves>), dim3((unsigned)merge_items), dim3(64 * kWideMergeWaves), 0,
+                       stream, p);
   } else {
     hipLaunchKernelGGL((merge_kernel<D, 1>), dim3((unsigned)((merge_items + kWavesPerBlock - 1) / kWavesPerBlock)),
                        dim3(kBlockThreads), 0, stream, p);
