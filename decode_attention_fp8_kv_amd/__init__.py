@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "KV_FP8_E4M3", "KV_BF16", "ABORT_TAG_MISMATCH", "ABORT_BAD_METADATA", "Fp8KvError",
-    "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn",
+    "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn", "paged_decode_step",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
     "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free", "kv_absmax_scale",
     "kv_absmax_scale_kv",
@@ -77,6 +77,9 @@ def load_library() -> ctypes.CDLL:
     lib.paged_decode_attn.restype = c.c_int
     lib.paged_decode_attn.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, vp, sz, i32, i32,
                                       i32, i32, i32, i32, f32, i32, vp]
+    lib.paged_decode_step.restype = c.c_int
+    lib.paged_decode_step.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp,
+                                      vp, sz, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
     lib.kv_quant_append_checked.restype = c.c_int
     lib.kv_quant_append_checked.argtypes = [vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, i32, i32, i32, i32,
                                             i32, i32, vp, vp, vp, vp]
@@ -207,6 +210,50 @@ def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flag
         batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_blocks),
         _stream_handle(dev, stream))
     _check("paged_decode_attn", status)
+
+
+def _event_handle(ev):
+    """The hipEvent_t of a torch.cuda.Event (created by recording it once if needed), or None."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record()
+    return ctypes.c_void_p(ev.cuda_event)
+
+
+def paged_decode_step(k_new, v_new, row_seq, row_pos, q, k_cache, v_cache, page_table, seq_lens, out, abort_flags,
+                      workspace, *, kv_dtype=KV_FP8_E4M3, k_scale=1.0, v_scale=1.0, page_tags=None,
+                      expected_tags=None, softmax_scale=None, num_blocks=0, decode_events=None, stream=None):
+    """One decode step: kv_quant_append of the new rows ``k_new/v_new [n_rows, Hkv, D]``, then
+    paged_decode_attn, with the page check (tags on) run inside the append's launch.  Results are
+    bit-identical to the two calls.  ``decode_events``: optional pair of torch.cuda.Event recorded
+    right before and right after the decode kernel.  See ``paged_decode_step`` in ``include/fp8kv.h``."""
+    dev = q.device
+    batch, hq, d = q.shape
+    num_pages, hkv, page_size, _ = k_cache.shape
+    max_pages = page_table.shape[1]
+    n_rows = k_new.shape[0]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out.shape != q.shape or abort_flags.numel() != batch or page_table.shape[0] != batch:
+        raise ValueError("shape mismatch")
+    if tuple(k_new.shape[1:]) != (hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between rows and caches")
+    if row_seq.numel() != n_rows or row_pos.numel() != n_rows:
+        raise ValueError("row_seq/row_pos must have n_rows entries")
+    ev0, ev1 = (None, None) if decode_events is None else decode_events
+    status = load_library().paged_decode_step(
+        _ptr(k_new, _BF16, "k_new", dev), _ptr(v_new, _BF16, "v_new", dev), _ptr(row_seq, _I32, "row_seq", dev),
+        _ptr(row_pos, _I32, "row_pos", dev), n_rows,
+        _ptr(q, _BF16, "q", dev), _ptr(k_cache, _CACHE[kv_dtype], "k_cache", dev),
+        _ptr(v_cache, _CACHE[kv_dtype], "v_cache", dev), kv_dtype, float(k_scale), float(v_scale),
+        _ptr(page_table, _I32, "page_table", dev), max_pages, _ptr(seq_lens, _I32, "seq_lens", dev),
+        _ptr(page_tags, _U32, "page_tags", dev), _ptr(expected_tags, _U32, "expected_tags", dev),
+        _ptr(out, _BF16, "out", dev), _ptr(abort_flags, (torch.uint8,), "abort_flags", dev),
+        _ptr(workspace, (torch.uint8,), "workspace", dev), workspace.numel(),
+        batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_blocks),
+        _event_handle(ev0), _event_handle(ev1), _stream_handle(dev, stream))
+    _check("paged_decode_step", status)
 
 
 def kv_quant_append_checked(k_new, v_new, row_seq, row_pos, page_table, k_scale, v_scale, k_cache, v_cache,

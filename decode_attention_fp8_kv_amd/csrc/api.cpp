@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -36,7 +37,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) &
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
-constexpr int64_t kComputeUnits = 256;    // MI355X; the default grid keeps every block resident
+constexpr int32_t kDefaultComputeUnits = 256;  // MI355X's count, if the device cannot be queried
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_compute_units[kMaxDevices];  // 0 = not queried yet
 constexpr int32_t kBlocksPerCu = 1;        // 4 waves per CU stream as fast as 8 and split the work less
 constexpr int64_t kMinTilesPerWave = 4;   // below this, fewer waves: merge cost beats parallelism
 constexpr int64_t kMaxBlocks = 65535;
@@ -51,13 +54,32 @@ int64_t max_total_tiles(int32_t batch, int32_t num_kv_heads, int32_t page_size, 
 
 }  // namespace
 
+// The default grids keep every block resident: one workgroup per compute unit.  A partitioned device
+// (e.g. a CPX-mode MI355X that shows 32 CUs) gets a grid of its own size.
+int32_t device_compute_units() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultComputeUnits;
+  }
+  int32_t cus = g_compute_units[dev].load(std::memory_order_relaxed);
+  if (cus > 0) return cus;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = kDefaultComputeUnits;
+  }
+  g_compute_units[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 int32_t plan_blocks(int32_t batch, int32_t num_kv_heads, int32_t page_size, int32_t max_pages, int32_t num_blocks,
                     int32_t blocks_per_cu) {
   int64_t nb = num_blocks;
   if (nb <= 0) {
     const int64_t bound = max_total_tiles(batch, num_kv_heads, page_size, max_pages);
     const int64_t per_block = kMinTilesPerWave * kWavesPerBlock;
-    nb = std::min(kComputeUnits * blocks_per_cu, (bound + per_block - 1) / per_block);
+    nb = std::min((int64_t)device_compute_units() * blocks_per_cu, (bound + per_block - 1) / per_block);
   }
   return (int32_t)std::max<int64_t>(1, std::min(nb, kMaxBlocks));
 }
@@ -102,12 +124,13 @@ const char* fp8kv_status_string(int status) {
 const char* fp8kv_last_hip_error(void) { return g_last_hip_error; }
 
 namespace {
-int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
-                      const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
-                      void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t page_size, int32_t kv_dtype, const uint32_t* page_tags,
-                      const uint32_t* expected_tags, uint8_t* row_status, const float* k_scale_dev,
-                      const float* v_scale_dev, void* stream) {
+// Argument checks and parameters of an append; FP8KV_OK or the status to return (nothing launched).
+int append_setup(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
+                 const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
+                 void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t page_size, int32_t kv_dtype, const uint32_t* page_tags,
+                 const uint32_t* expected_tags, uint8_t* row_status, const float* k_scale_dev,
+                 const float* v_scale_dev, AppendParams& p) {
   if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
   if (n_rows < 0 || batch <= 0 || max_pages <= 0 || num_pages <= 0 || num_kv_heads <= 0 || num_kv_heads > 65535)
     return FP8KV_ERR_SHAPE;
@@ -122,7 +145,6 @@ int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return FP8KV_ERR_ALIGN;
 
-  AppendParams p;
   p.k_scale_dev = k_scale_dev;
   p.v_scale_dev = v_scale_dev;
   p.k_new = k_new;
@@ -144,6 +166,20 @@ int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_
   p.num_kv_heads = num_kv_heads;
   p.head_dim = head_dim;
   p.log2_page_size = l2ps;
+  return FP8KV_OK;
+}
+
+int quant_append_impl(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
+                      const int32_t* page_table, int32_t batch, int32_t max_pages, float k_scale, float v_scale,
+                      void* k_cache, void* v_cache, int32_t num_pages, int32_t n_rows, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, int32_t kv_dtype, const uint32_t* page_tags,
+                      const uint32_t* expected_tags, uint8_t* row_status, const float* k_scale_dev,
+                      const float* v_scale_dev, void* stream) {
+  AppendParams p{};
+  const int st = append_setup(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, k_scale, v_scale,
+                              k_cache, v_cache, num_pages, n_rows, num_kv_heads, head_dim, page_size, kv_dtype,
+                              page_tags, expected_tags, row_status, k_scale_dev, v_scale_dev, p);
+  if (st != FP8KV_OK || n_rows == 0) return st;
   return record_hip(launch_quant_append(p, kv_dtype, static_cast<hipStream_t>(stream)));
 }
 
@@ -289,12 +325,14 @@ int paged_decode_attn_path(int32_t num_q_heads, int32_t num_kv_heads) {
   return num_q_heads / num_kv_heads >= 5 ? 1 : 0;
 }
 
-int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, float k_scale,
-                      float v_scale, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
-                      const uint32_t* page_tags, const uint32_t* expected_tags, uint16_t* out, uint8_t* abort_flags,
-                      void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
-                      float softmax_scale, int32_t num_blocks, void* stream) {
+namespace {
+// Argument checks and parameters of a decode call; FP8KV_OK or the status to return (nothing launched).
+int decode_setup(const uint16_t* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, float k_scale,
+                 float v_scale, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                 const uint32_t* page_tags, const uint32_t* expected_tags, uint16_t* out, uint8_t* abort_flags,
+                 void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                 int32_t head_dim, int32_t page_size, int32_t num_pages, float softmax_scale, int32_t num_blocks,
+                 DecodeParams& p, bool& mfma) {
   if (kv_dtype != FP8KV_KV_FP8_E4M3 && kv_dtype != FP8KV_KV_BF16) return FP8KV_ERR_UNSUPPORTED;
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_pages <= 0 || num_pages <= 0 || num_blocks < 0)
     return FP8KV_ERR_SHAPE;
@@ -312,17 +350,16 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   if (kv_dtype == FP8KV_KV_FP8_E4M3 && (!finite_positive(k_scale) || !finite_positive(v_scale)))
     return FP8KV_ERR_SCALE;
   if (!std::isfinite(softmax_scale)) return FP8KV_ERR_SCALE;
-  if (!aligned(q, 16) || !aligned(out, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+  if (!aligned(q, 16) || !aligned(out, 8) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(workspace, 256))
     return FP8KV_ERR_ALIGN;
-  const bool mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
+  mfma = paged_decode_attn_path(num_q_heads, num_kv_heads) == 1;
   // one resident block (4 waves) per CU by default: every decode kernel runs one wave per SIMD
   const int32_t nb = plan_blocks(batch, num_kv_heads, page_size, max_pages, num_blocks, kBlocksPerCu);
   const WorkspaceLayout ws = workspace_layout(batch, num_q_heads, num_kv_heads, head_dim, max_pages, nb);
   if (workspace_bytes < ws.total) return FP8KV_ERR_WORKSPACE;
 
   const double log2e = 1.4426950408889634;
-  DecodeParams p;
   p.q = q;
   p.k_cache = static_cast<const uint8_t*>(k_cache);
   p.v_cache = static_cast<const uint8_t*>(v_cache);
@@ -335,6 +372,7 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
   uint8_t* base = static_cast<uint8_t*>(workspace);
   p.check_bits = base + ws.check_bits;
   p.check_chunks = check_chunks(max_pages);
+  p.checked = page_tags != nullptr ? 1 : 0;
   p.seg_desc = reinterpret_cast<uint64_t*>(base + ws.seg_desc);
   p.part_ml = reinterpret_cast<float*>(base + ws.part_ml);
   p.part_acc = reinterpret_cast<float*>(base + ws.part_acc);
@@ -353,7 +391,59 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
     p.qk_scale_log2 = (float)((double)softmax_scale * log2e);
     p.v_scale = 1.0f;
   }
-  return record_hip(launch_decode(p, kv_dtype, head_dim, mfma, static_cast<hipStream_t>(stream)));
+  return FP8KV_OK;
+}
+}  // namespace
+
+int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache, int32_t kv_dtype, float k_scale,
+                      float v_scale, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                      const uint32_t* page_tags, const uint32_t* expected_tags, uint16_t* out, uint8_t* abort_flags,
+                      void* workspace, size_t workspace_bytes, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+                      float softmax_scale, int32_t num_blocks, void* stream) {
+  DecodeParams p{};
+  bool mfma = false;
+  const int st = decode_setup(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_table, max_pages, seq_lens,
+                              page_tags, expected_tags, out, abort_flags, workspace, workspace_bytes, batch,
+                              num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale, num_blocks,
+                              p, mfma);
+  if (st != FP8KV_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.checked) {
+    const int e = record_hip(launch_page_check(p, s));
+    if (e != FP8KV_OK) return e;
+  }
+  return record_hip(launch_decode(p, kv_dtype, head_dim, mfma, s));
+}
+
+int paged_decode_step(const uint16_t* k_new, const uint16_t* v_new, const int32_t* row_seq, const int32_t* row_pos,
+                      int32_t n_rows, const uint16_t* q, void* k_cache, void* v_cache, int32_t kv_dtype,
+                      float k_scale, float v_scale, const int32_t* page_table, int32_t max_pages,
+                      const int32_t* seq_lens, const uint32_t* page_tags, const uint32_t* expected_tags,
+                      uint16_t* out, uint8_t* abort_flags, void* workspace, size_t workspace_bytes, int32_t batch,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t num_pages, float softmax_scale, int32_t num_blocks, void* decode_begin_event,
+                      void* decode_end_event, void* stream) {
+  DecodeParams p{};
+  bool mfma = false;
+  int st = decode_setup(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_table, max_pages, seq_lens, page_tags,
+                        expected_tags, out, abort_flags, workspace, workspace_bytes, batch, num_q_heads, num_kv_heads,
+                        head_dim, page_size, num_pages, softmax_scale, num_blocks, p, mfma);
+  if (st != FP8KV_OK) return st;
+  AppendParams a{};
+  st = append_setup(k_new, v_new, row_seq, row_pos, page_table, batch, max_pages, k_scale, v_scale, k_cache, v_cache,
+                    num_pages, n_rows, num_kv_heads, head_dim, page_size, kv_dtype, nullptr, nullptr, nullptr, nullptr,
+                    nullptr, a);
+  if (st != FP8KV_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int e = FP8KV_OK;
+  if (p.checked)
+    e = record_hip(launch_append_check(a, p, kv_dtype, s));
+  else if (n_rows > 0)
+    e = record_hip(launch_quant_append(a, kv_dtype, s));
+  if (e != FP8KV_OK) return e;
+  return record_hip(launch_decode(p, kv_dtype, head_dim, mfma, s, static_cast<hipEvent_t>(decode_begin_event),
+                                  static_cast<hipEvent_t>(decode_end_event)));
 }
 
 }  // extern "C"

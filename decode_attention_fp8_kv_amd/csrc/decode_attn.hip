@@ -17,15 +17,21 @@
 //
 // Kernels of one call
 // -------------------
-// 1. check_kernel (one block per 1024 page-table slots of a sequence)
-//    checks every page slot of every sequence -- page id in range, tag equal
-//    to the expected tag -- and the length.
+// 1. With tags on, a page check (check_block in page_check.hpp: one block per
+//    1024 page-table slots of a sequence) checks every used page slot of
+//    every sequence -- page id in range, tag equal to the expected tag -- and
+//    the length.  It is its own kernel in paged_decode_attn and shares the
+//    first kernel of a decode step with the append's blocks.
 // 2. decode_kernel writes the abort flags and streams K/V for the
-//    sequences that passed.
-// 3. merge_kernel combines the partial results of split segments.
-// The check comes first so that an aborted sequence costs 12 bytes per page
-// (id, tag, expected tag) instead of its K/V, and is left out of the work
-// partition, which keeps the shares of the other sequences balanced.
+//    sequences that passed.  With tags off no check ran: the schedule checks
+//    the lengths, and every round of page ids a wave loads is range-checked
+//    before any of its pages is read (a failing piece stops and reports).
+// 3. merge_kernel combines the partial results of split segments and adds
+//    the bits of pieces that failed the range check.
+// With tags on the check comes first so that an aborted sequence costs 12
+// bytes per page (id, tag, expected tag) instead of its K/V, and is left out
+// of the work partition, which keeps the shares of the other sequences
+// balanced.
 //
 // Work decomposition
 // ------------------
@@ -67,12 +73,11 @@
 // v_scale the final output, so dequantization itself adds no rounding.
 #include "common.hpp"
 #include "internal.hpp"
+#include "page_check.hpp"
 
 namespace fp8kv {
 namespace {
 
-constexpr uint32_t kAbortTag = 1u;
-constexpr uint32_t kAbortMeta = 2u;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // ------------------------------------------------------------------------
@@ -602,8 +607,11 @@ __device__ __forceinline__ void compute_tile(typename WaveState<KV, D, GM, MFMA>
   }
 }
 
+// Returns false (and stops) if a round's page ids include one outside
+// [0, num_pages): no page of that round is read.  With tags on the page
+// check already excluded such sequences, so this never fails then.
 template <int KV, int D, int GM, bool MFMA>
-__device__ __forceinline__ void run_wave(const DecodeParams& p, int b, int g, int L, int first_tile, int n_wave_tiles,
+__device__ __forceinline__ bool run_wave(const DecodeParams& p, int b, int g, int L, int first_tile, int n_wave_tiles,
                                          typename WaveState<KV, D, GM, MFMA>::T& st, int lane, uint8_t* vstage) {
   constexpr bool kVlds = MFMA && KV == 0;  // FP8 V streams through LDS
   using Tile = typename WaveState<KV, D, GM, MFMA>::Tile;
@@ -613,7 +621,6 @@ __device__ __forceinline__ void run_wave(const DecodeParams& p, int b, int g, in
   const int n_pages_b = (L + (1 << log2ps) - 1) >> log2ps;
   const int64_t pt_row = (int64_t)b * p.max_pages;
 
-  // The sequence passed the page check, so every page id read here is in range.
   for (int r0 = 0; r0 < n_wave_tiles; r0 += round_tiles) {
     const int rt = min(round_tiles, n_wave_tiles - r0);
     // lane j -> wave page j of this round
@@ -622,6 +629,7 @@ __device__ __forceinline__ void run_wave(const DecodeParams& p, int b, int g, in
     const int lp = log2ps < 6 ? (tile_j << ppt_log2) + (lane & ((1 << ppt_log2) - 1)) : (tile_j << 6) >> log2ps;
     const bool used = jt < rt && lp < n_pages_b;
     const int pid = used ? p.page_table[pt_row + lp] : 0;
+    if (__ballot(used && (pid < 0 || pid >= p.num_pages)) != 0) return false;
     PageRound pr;
     pr.log2ps = log2ps;
     pr.ppt_log2 = ppt_log2;
@@ -684,6 +692,7 @@ __device__ __forceinline__ void run_wave(const DecodeParams& p, int b, int g, in
     }
     }
   }
+  return true;
 }
 
 // ------------------------------------------------------------------------
@@ -744,6 +753,14 @@ __device__ __forceinline__ void wave_publish(MfmaState<KV, D>& st, const DecodeP
     }
     if (lane < 16) *reinterpret_cast<f32x2_t*>(p.part_ml + (slot * G + h) * 2) = f32x2_t{st.m, l};
   }
+}
+
+// A partial piece whose page ids failed the range check publishes m = +inf
+// for every head (no valid partial has it); the merge then writes no output
+// for the segment and adds the abort bit.
+__device__ __forceinline__ void wave_publish_abort(const DecodeParams& p, int64_t slot, int lane) {
+  for (int h = lane; h < p.group; h += 64)
+    *reinterpret_cast<f32x2_t*>(p.part_ml + (slot * p.group + h) * 2) = f32x2_t{__builtin_huge_valf(), 0.f};
 }
 
 // VALU family: merge the 8 token slots (lanes differing in bits 3..5) first.
@@ -838,6 +855,9 @@ __device__ __forceinline__ void wave_publish(ValuState<KV, D, GM>& st, const Dec
 // the partials visible to it, so no wave ever synchronizes with another.
 // ------------------------------------------------------------------------
 constexpr int64_t kSeqCount = int64_t(1) << 44;  // pass 1 packs a sequence count above the tile count
+// A segment descriptor with this bit: a page id of the segment failed the
+// decode's range check (tags off); nothing was written for it.
+constexpr uint64_t kDescAbortMeta = uint64_t(1) << 63;
 constexpr int kPieceUnits = 1;                    // schedule units a segment charges at its start
 constexpr int64_t kMinTilesForCharge = 16;        // tiles per wave from which the charge applies
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nw) { return w * total / nw; }
@@ -920,12 +940,13 @@ __device__ __forceinline__ void wave_piece(const DecodeParams& p, uint8_t* vstag
     }
   }
 
-  run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo, t_hi - t_lo, st, lane, vstage);
+  const bool ok = run_wave<KV, D, GM, MFMA>(p, b, g, L, t_lo, t_hi - t_lo, st, lane, vstage);
   const int64_t seg = (int64_t)b * p.num_kv_heads + g;
   if (t_lo == 0 && t_hi == T) {
-    // The whole segment is here: finish it.
-    if (lane == 0) p.seg_desc[seg] = 0;
-    wave_output(st, p, ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D, lane);
+    // The whole segment is here: finish it (or, if one of its page ids was
+    // out of range, write nothing and tell the merge kernel to flag it).
+    if (lane == 0) p.seg_desc[seg] = ok ? 0 : kDescAbortMeta;
+    if (ok) wave_output(st, p, ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D, lane);
     return;
   }
   if (t_lo == 0 && lane == 0) {
@@ -936,64 +957,26 @@ __device__ __forceinline__ void wave_piece(const DecodeParams& p, uint8_t* vstag
     p.seg_desc[seg] = first_slot | ((uint64_t)n_part << 32);
   }
   // A partial piece: publish it; the merge kernel combines the partials.
-  wave_publish(st, p, 2 * w + ((seg_lo + t_lo) == r0 ? 0 : 1), lane);
+  const int64_t slot = 2 * w + ((seg_lo + t_lo) == r0 ? 0 : 1);
+  if (ok)
+    wave_publish(st, p, slot, lane);
+  else
+    wave_publish_abort(p, slot, lane);
 }
 
 // ------------------------------------------------------------------------
-// The page check, before any K/V is read: one block per (1024-slot chunk of
-// the page table, sequence).  Every page slot j < ceil(L / page_size) of
-// sequence b is checked: the id must lie in [0, num_pages) (else bit
-// kAbortMeta) and, when tags are on, the page's current tag must equal the
-// tag the sequence recorded for that slot (else bit kAbortTag); a length
-// outside [1, max_pages * page_size] is kAbortMeta.  Each block writes its
-// chunk's bits; the decode kernel ORs a sequence's chunks into its abort
-// flag.  Page ids and expected tags are loaded for the whole chunk of the
-// table row (always in bounds) while the length is still in flight, so the
-// check costs two dependent loads.
+// The page check of a call with tags on (see page_check.hpp).
 // ------------------------------------------------------------------------
-constexpr int kCheckUnroll = 4;                             // slots per thread
-constexpr int kCheckChunk = kCheckUnroll * kBlockThreads;   // slots per block
-static_assert(kCheckChunk == kCheckSlots, "the host sizes the check grid with kCheckSlots");
-
 __global__ __launch_bounds__(kBlockThreads) void check_kernel(DecodeParams p) {
-  const int c = blockIdx.x, b = blockIdx.y;
-  const int L = p.seq_lens[b];
-  const int64_t row = (int64_t)b * p.max_pages;
-  const bool tags_on = p.page_tags != nullptr;
-  int pid[kCheckUnroll];
-  uint32_t expected[kCheckUnroll];
-#pragma unroll
-  for (int u = 0; u < kCheckUnroll; ++u) {
-    const int j = c * kCheckChunk + u * kBlockThreads + threadIdx.x;
-    pid[u] = j < p.max_pages ? p.page_table[row + j] : 0;
-    expected[u] = (tags_on && j < p.max_pages) ? p.expected_tags[row + j] : 0u;
-  }
-  const int max_tokens = p.max_pages << p.log2_page_size;
-  uint32_t bits = 0;
-  if (L < 1 || L > max_tokens) {
-    bits = kAbortMeta;
-  } else {
-    const int n_pages = (L + (1 << p.log2_page_size) - 1) >> p.log2_page_size;
-#pragma unroll
-    for (int u = 0; u < kCheckUnroll; ++u) {
-      const int j = c * kCheckChunk + u * kBlockThreads + threadIdx.x;
-      if (j >= n_pages) continue;
-      if (pid[u] < 0 || pid[u] >= p.num_pages)
-        bits |= kAbortMeta;
-      else if (tags_on && p.page_tags[pid[u]] != expected[u])
-        bits |= kAbortTag;
-    }
-  }
-  const int any_tag = __syncthreads_or((int)(bits & kAbortTag));
-  const int any_meta = __syncthreads_or((int)(bits & kAbortMeta));
-  if (threadIdx.x == 0)
-    p.check_bits[(int64_t)b * p.check_chunks + c] = (uint8_t)((any_tag ? kAbortTag : 0u) | (any_meta ? kAbortMeta : 0u));
+  check_block(p, blockIdx.x, blockIdx.y);
 }
 
-// Abort bits of sequence b: the OR of its chunks' check results.
-__device__ __forceinline__ uint32_t seq_abort_bits(const DecodeParams& p, int b) {
-  uint32_t bits = 0;
-  for (int c = 0; c < p.check_chunks; ++c) bits |= p.check_bits[(int64_t)b * p.check_chunks + c];
+// Abort bits of sequence b known before the decode: the OR of its chunks'
+// check results when the page check ran, plus the length check.
+__device__ __forceinline__ uint32_t seq_abort_bits(const DecodeParams& p, int b, int L, int max_tokens) {
+  uint32_t bits = (L < 1 || L > max_tokens) ? kAbortMeta : 0u;
+  if (p.checked)
+    for (int c = 0; c < p.check_chunks; ++c) bits |= p.check_bits[(int64_t)b * p.check_chunks + c];
   return bits;
 }
 
@@ -1018,8 +1001,8 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
   int64_t mine = 0;
   int L0 = 0, T0 = 0;  // length and tiles of sequence `lane` (the first chunk of pass 2)
   for (int b = lane; b < p.batch; b += 64) {
-    const uint32_t bits = seq_abort_bits(p, b);
     const int Lb = p.seq_lens[b];
+    const uint32_t bits = seq_abort_bits(p, b, Lb, max_tokens);
     const int T = seq_tiles(Lb, max_tokens, bits);
     if (b == lane) {
       L0 = Lb;
@@ -1056,7 +1039,7 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
     const int b = c + lane;
     // the first 64 sequences were read in pass 1: no second trip to memory
     const int Lc = c == 0 ? L0 : (b < p.batch ? p.seq_lens[b] : 0);
-    const int T = c == 0 ? T0 : (b < p.batch ? seq_tiles(Lc, max_tokens, seq_abort_bits(p, b)) : 0);
+    const int T = c == 0 ? T0 : (b < p.batch ? seq_tiles(Lc, max_tokens, seq_abort_bits(p, b, Lc, max_tokens)) : 0);
     const int U = T > 0 ? T + delta : 0;  // units per KV head of sequence b
     const int64_t incl = wave_inclusive_scan64(U);
     const int64_t excl = carry + incl - U;
@@ -1091,7 +1074,12 @@ __global__ __launch_bounds__(kBlockThreads, 1) void decode_kernel(DecodeParams p
 // finished inside one wave were written by the decode kernel, and aborted
 // sequences have no descriptor; the others' partials are combined by
 // log-sum-exp: M = max m_a, L = sum l_a 2^(m_a - M),
-// o = v_scale * sum acc_a 2^(m_a - M) / L, rounded to BF16.  The item's
+// o = v_scale * sum acc_a 2^(m_a - M) / L, rounded to BF16.  A segment with
+// a piece that failed the decode's page-id range check (descriptor bit 63,
+// or a partial with m = +inf) gets no output, and the item of its sequence's
+// first KV head and first query head adds kAbortMeta to the abort flag (the
+// decode kernel wrote the flag's other bits; every KV head's pieces read the
+// same pages, so each segment reaches the same verdict).  The item's
 // waves split its partials; lanes hold the statistics of up to 64 partials
 // at a time and the head's output dims; each partial's accumulator row is
 // one coalesced load per wave, kMergeUnroll of them in flight per lane; with
@@ -1121,8 +1109,13 @@ __global__ __launch_bounds__(64 * (WPI > kWavesPerBlock ? WPI : kWavesPerBlock))
   const int h = (int)(item - seg * G);
   const int b = (int)(seg / p.num_kv_heads), g = (int)(seg - (int64_t)b * p.num_kv_heads);
   const uint64_t desc = p.seg_desc[seg];
+  const bool flag_writer = g == 0 && h == 0 && sub == 0 && lane == 0;
+  if (desc & kDescAbortMeta) {  // a whole segment that failed the range check
+    if (flag_writer) p.abort_flags[b] |= (uint8_t)kAbortMeta;
+    return;
+  }
   const int n_arr = (int)(desc >> 32);
-  if (n_arr < 2) return;  // finished inside one wave, or aborted
+  if (n_arr < 2) return;  // finished inside one wave, or aborted by the page check
   const int64_t first_slot = (uint32_t)desc;
   const int64_t first = first_slot >> 1;
   // a descriptor always names slots of this call's waves; never read past them
@@ -1149,6 +1142,10 @@ __global__ __launch_bounds__(64 * (WPI > kWavesPerBlock ? WPI : kWavesPerBlock))
     M = kNegInf;
 #pragma unroll
     for (int i = 0; i < WPI; ++i) M = __builtin_fmaxf(M, part_m[w0 + i]);
+  }
+  if (M == __builtin_huge_valf()) {  // a piece failed the range check (uniform over the item's waves)
+    if (flag_writer) p.abort_flags[b] |= (uint8_t)kAbortMeta;
+    return;
   }
 
   // 64 partials at a time: lane j's weight 2^(m - M) is read by every lane
@@ -1222,13 +1219,18 @@ __global__ __launch_bounds__(64 * (WPI > kWavesPerBlock ? WPI : kWavesPerBlock))
 }
 
 template <int KV, int D, int GM, bool MFMA>
-hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(check_kernel, dim3(p.check_chunks, p.batch), dim3(kBlockThreads), 0, stream, p);
-  hipError_t e0 = hipGetLastError();
-  if (e0 != hipSuccess) return e0;
+hipError_t launch_one(const DecodeParams& p, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0 != nullptr) {
+    const hipError_t e = hipEventRecord(ev0, stream);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((decode_kernel<KV, D, GM, MFMA>), dim3(p.num_blocks), dim3(kBlockThreads), 0, stream, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (ev1 != nullptr) {
+    const hipError_t e1 = hipEventRecord(ev1, stream);
+    if (e1 != hipSuccess) return e1;
+  }
   const int64_t merge_items = (int64_t)p.batch * p.num_q_heads;  // one per query head
   // Segments split into many partials (more waves than 16 per segment when
   // every segment is as long as the page table allows) get kWideMergeWaves
@@ -1245,22 +1247,28 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
 }
 
 template <int KV, int D>
-hipError_t launch_dtype_dim(const DecodeParams& p, bool mfma, hipStream_t stream) {
-  if (mfma) return launch_one<KV, D, 16, true>(p, stream);
-  if (p.group <= 1) return launch_one<KV, D, 1, false>(p, stream);
-  if (p.group <= 2) return launch_one<KV, D, 2, false>(p, stream);
-  return launch_one<KV, D, 4, false>(p, stream);
+hipError_t launch_dtype_dim(const DecodeParams& p, bool mfma, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (mfma) return launch_one<KV, D, 16, true>(p, stream, ev0, ev1);
+  if (p.group <= 1) return launch_one<KV, D, 1, false>(p, stream, ev0, ev1);
+  if (p.group <= 2) return launch_one<KV, D, 2, false>(p, stream, ev0, ev1);
+  return launch_one<KV, D, 4, false>(p, stream, ev0, ev1);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma, hipStream_t stream) {
+hipError_t launch_page_check(const DecodeParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(check_kernel, dim3(p.check_chunks, p.batch), dim3(kBlockThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma, hipStream_t stream,
+                         hipEvent_t decode_begin, hipEvent_t decode_end) {
   if (kv_dtype == 0) {
-    if (head_dim == 64) return launch_dtype_dim<0, 64>(p, mfma, stream);
-    return launch_dtype_dim<0, 128>(p, mfma, stream);
+    if (head_dim == 64) return launch_dtype_dim<0, 64>(p, mfma, stream, decode_begin, decode_end);
+    return launch_dtype_dim<0, 128>(p, mfma, stream, decode_begin, decode_end);
   }
-  if (head_dim == 64) return launch_dtype_dim<1, 64>(p, mfma, stream);
-  return launch_dtype_dim<1, 128>(p, mfma, stream);
+  if (head_dim == 64) return launch_dtype_dim<1, 64>(p, mfma, stream, decode_begin, decode_end);
+  return launch_dtype_dim<1, 128>(p, mfma, stream, decode_begin, decode_end);
 }
 
 }  // namespace fp8kv

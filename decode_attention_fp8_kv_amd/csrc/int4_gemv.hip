@@ -55,8 +55,8 @@ constexpr int kI4RingLds = 4;       // ring depth when the activations sit in LD
 // tile-times wins, the larger on a tie (each activation block then feeds
 // more weight rows).  At 28,672 rows (1,792 tiles), 7 tiles per workgroup
 // make 256 workgroups and one round where 4 made 448 and two: M = 16 went
-// from 36 to 28 us and M = 64 from 84 to 60 us.
-constexpr int kI4Cus = 256;  // MI355X compute units
+// from 36 to 28 us and M = 64 from 84 to 60 us.  The CU count is the
+// device's own (device_compute_units).
 
 // One word of 8 weights -> 8 bf16 values 1 + (q + 8)/16 in natural k order.
 // Each pair: shift the two nibbles to bits 3..6 / 19..22, keep them, and
@@ -311,12 +311,13 @@ hipError_t launch_int4_pack(const uint32_t* w_rows, const uint16_t* s_rows, uint
 
 namespace {
 
-// Tiles per workgroup on the register path (see kI4Cus).
+// Tiles per workgroup on the register path (see the register-path comment above).
 int pick_tiles(int64_t tiles) {
+  const int64_t cus = device_compute_units();
   int best = 7;
   int64_t best_cost = INT64_MAX;
   for (const int ns : {7, 4, 2}) {
-    const int64_t rounds = ((tiles + ns - 1) / ns + kI4Cus - 1) / kI4Cus;
+    const int64_t rounds = ((tiles + ns - 1) / ns + cus - 1) / cus;
     if (rounds * ns < best_cost) {
       best_cost = rounds * ns;
       best = ns;

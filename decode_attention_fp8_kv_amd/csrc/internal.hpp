@@ -62,13 +62,17 @@ struct DecodeParams {
   uint16_t* out;                    // bf16 [B][Hq][D]
   uint8_t* abort_flags;             // [B]
   uint8_t* check_bits;              // [B][check_chunks] abort bits found by the page check
-  uint64_t* seg_desc;               // [B*Hkv] first partial slot | number of partials << 32 (< 2: none)
+  uint64_t* seg_desc;               // [B*Hkv] first partial slot | number of partials << 32 (< 2: none);
+                                    // bit 63: a page id failed the decode's range check
   float* part_ml;                   // [2*waves][G][2]  running max (log2 domain), sum
   float* part_acc;                  // [2*waves][G][D]  unnormalized output
   int32_t batch, num_q_heads, num_kv_heads, group, max_pages, num_pages;
   int32_t log2_page_size;
   int32_t num_blocks;               // grid size; each of its 4*num_blocks waves owns an equal share
   int32_t check_chunks;             // page-check blocks per sequence (1024 page slots each)
+  int32_t checked;                  // 1: check_bits hold this call's page check (tags on); 0: no
+                                    // check ran, lengths are checked in the decode's schedule and
+                                    // page ids as each round of pages is loaded
   float qk_scale_log2;              // softmax_scale * k_scale * log2(e)
   float v_scale;                    // folded into the final normalization
 };
@@ -96,7 +100,18 @@ hipError_t launch_pool_free(const PoolParams& p, hipStream_t stream);
 hipError_t launch_int4_gemv(const Int4GemvParams& p, hipStream_t stream);
 hipError_t launch_int4_pack(const uint32_t* w_rows, const uint16_t* s_rows, uint32_t* w_tiles, uint16_t* s_tiles,
                             int32_t n, int32_t k, hipStream_t stream);
-hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma,
-                         hipStream_t stream);
+// Page check alone (one block per 1024-slot chunk of a sequence); writes check_bits.
+hipError_t launch_page_check(const DecodeParams& p, hipStream_t stream);
+// The append's rows and the page check in one launch (a decode step's first kernel): the append's
+// blocks come first, then one block per (chunk, sequence) of the check.
+hipError_t launch_append_check(const AppendParams& a, const DecodeParams& d, int kv_dtype, hipStream_t stream);
+// Decode + merge.  Events, when not null, are recorded on the stream right before the decode kernel
+// and right after it (before the merge).
+hipError_t launch_decode(const DecodeParams& p, int kv_dtype, int head_dim, bool mfma, hipStream_t stream,
+                         hipEvent_t decode_begin = nullptr, hipEvent_t decode_end = nullptr);
+
+// Compute units of the current device, queried once per device (256, MI355X's count, if the query
+// fails, e.g. when no device is visible to a host-only caller).
+int32_t device_compute_units();
 
 }  // namespace fp8kv

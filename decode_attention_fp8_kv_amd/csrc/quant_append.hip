@@ -13,8 +13,15 @@
 // and stores are fully coalesced; a row of one head is one contiguous run
 // of head_dim elements in its page.  Sixteen independent divisions per
 // tensor and thread keep the IEEE division's dependency chains overlapped.
+//
+// A decode step's first kernel (append_check_kernel) runs these rows and the
+// page check of the step's decode in one launch: the append writes only
+// cache bytes and the check reads only the page table, lengths and tags, so
+// the two are independent, and the check's blocks run beside the append's
+// instead of costing a launch of their own.
 #include "common.hpp"
 #include "internal.hpp"
+#include "page_check.hpp"
 
 namespace fp8kv {
 namespace {
@@ -36,10 +43,11 @@ __device__ __forceinline__ u32x4_t quant16(const u32x4_t (&in)[2], float s) {
   return out;
 }
 
+// Thread idx of the append: elements [16 c, 16 c + 16) of one row's
+// num_kv_heads * head_dim, c = idx % (num_kv_heads * head_dim / 16).
 template <int KV>
-__global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
+__device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t idx) {
   const int chunks_per_row = (p.num_kv_heads * p.head_dim) / kChunk;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (int64_t)p.n_rows * chunks_per_row) return;
   const int row = (int)(idx / chunks_per_row);
   const int e0 = (int)(idx - (int64_t)row * chunks_per_row) * kChunk;  // element within the row
@@ -94,17 +102,57 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
   }
 }
 
+template <int KV>
+__global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
+  append_chunk<KV>(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// Blocks [0, append_blocks): the append; then one block per (chunk c,
+// sequence b) of the page check, c fastest.  The branch is uniform per block,
+// as check_block's block-wide reductions require.
+template <int KV>
+__global__ __launch_bounds__(256) void append_check_kernel(AppendParams a, DecodeParams d, int64_t append_blocks) {
+  const int64_t blk = blockIdx.x;
+  if (blk < append_blocks) {
+    append_chunk<KV>(a, blk * 256 + threadIdx.x);
+    return;
+  }
+  const int64_t cb = blk - append_blocks;
+  check_block(d, (int)(cb % d.check_chunks), (int)(cb / d.check_chunks));
+}
+
+static_assert(kBlockThreads == 256, "the append and the check share a block size");
+
+int64_t append_blocks(const AppendParams& p) {
+  const int64_t threads = (int64_t)p.n_rows * ((p.num_kv_heads * p.head_dim) / kChunk);
+  return (threads + 255) / 256;
+}
+
 }  // namespace
 
 hipError_t launch_quant_append(const AppendParams& p, int kv_dtype, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.n_rows * ((p.num_kv_heads * p.head_dim) / kChunk);
-  if (threads == 0) return hipSuccess;
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = append_blocks(p);
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   if (kv_dtype == 0)
     hipLaunchKernelGGL(quant_append_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(quant_append_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_check(const AppendParams& a, const DecodeParams& d, int kv_dtype, hipStream_t stream) {
+  const int64_t na = append_blocks(a);
+  const int64_t total = na + (int64_t)d.check_chunks * d.batch;
+  if (total > 0x7FFFFFFF) {  // too many blocks for one 1-D grid: two launches
+    const hipError_t e = launch_quant_append(a, kv_dtype, stream);
+    if (e != hipSuccess) return e;
+    return launch_page_check(d, stream);
+  }
+  if (kv_dtype == 0)
+    hipLaunchKernelGGL(append_check_kernel<0>, dim3((unsigned)total), dim3(256), 0, stream, a, d, na);
+  else
+    hipLaunchKernelGGL(append_check_kernel<1>, dim3((unsigned)total), dim3(256), 0, stream, a, d, na);
   return hipGetLastError();
 }
 

@@ -15,21 +15,27 @@ Recipes (every random draw comes from a ``torch.Generator`` seeded per field):
 * ``tiny``    -- batch 2, 8/2 heads, D 64, pages of 16, lengths 100 and 257,
   K/V/Q ~ N(0,1), a 64-page pool, random uint32 tags with one mismatch
   injected into sequence 1; softmax scale 1/8.
-* ``latency`` -- batch 1, context 32768, a 512-page pool (permuted), all tags
-  valid.
+* ``latency`` -- batch 1, context 32768: 32767 tokens cached and the step's
+  new token appended at position 32767, so attention covers 32768 tokens in
+  a 512-page pool (permuted); all tags valid.
 * ``conc32``  -- batch 32, context lengths uniform in [4096, 32768]; 1% of the
   (head, dim) channels of K and of V (10 of 1024) are multiplied by 8; one
   new token per sequence is appended at position ``L0`` and attention runs
   over ``L0 + 1`` tokens; scales come from the cache before the append, so
   appended outliers can saturate.
-* ``conc64``  -- batch 64, lengths lognormal (median 12000, sigma 1.0),
-  rounded and clipped to [512, 65536]; the pool holds exactly the pages the
-  lengths need; 0.1% of pages are stale (their tag bumped after the fact).
-  With ``bf16_subset=True`` only the first 32 sequences are kept and the pool
-  is resized to fit them, as a BF16 cache of the same memory would force.
-* ``long``    -- batch 8, context 131072, K/V Student-t with 3 degrees of
-  freedom (so e4m3 saturation and subnormals occur); the scale is the 99.9th
-  percentile of |x| over a seeded 2^20-element sample, divided by 448; with
+* ``conc64``  -- batch 64, lengths ``L0`` lognormal (median 12000, sigma 1.0),
+  rounded and clipped to [512, 65536]; as in ``conc32`` one new token per
+  sequence is appended at ``L0`` and attention covers ``L0 + 1`` tokens; the
+  pool holds exactly the pages those lengths need; 0.1% of the pool's pages
+  are stale (their tag bumped after the fact).  With
+  ``bf16_same_memory=True`` the cache is BF16 in a pool of the same bytes
+  (half as many pages): sequences are admitted in order while their pages
+  fit -- the first 29 at the default seed -- and 0.1% of that pool's pages
+  are stale.
+* ``long``    -- batch 8, context 131072 (131071 cached + the step's new
+  token), K/V Student-t with 3 degrees of freedom (so e4m3 saturation and
+  subnormals occur); the scale is the 99.9th percentile of |x| over a seeded
+  2^20-element sample of the cached rows, divided by 448; with
   ``inject_tags=True`` each used (sequence, page) slot independently gets a
   mismatched expected tag with probability 1/1000.
 
@@ -192,7 +198,7 @@ CONFIG_NAMES = ("tiny", "latency", "conc32", "conc64", "long")
 DEFAULT_SEEDS = {"tiny": 1, "latency": 2, "conc32": 3, "conc64": 4, "long": 5}
 
 
-def make(name: str, seed: int | None = None, device="cpu", *, bf16_subset=False,
+def make(name: str, seed: int | None = None, device="cpu", *, bf16_same_memory=False,
          inject_tags=False, batch=None, context=None, long_scale="p999") -> Workload:
     """Build workload ``name`` on ``device`` ("cpu" or "cuda").
 
@@ -220,7 +226,8 @@ def make(name: str, seed: int | None = None, device="cpu", *, bf16_subset=False,
         g = _cpu_gen(seed, 0)
         if name == "latency":
             B = 1 if batch is None else batch
-            ctx = np.full(B, 32768 if context is None else context, dtype=np.int64)
+            ctx = np.full(B, (32768 if context is None else context) - 1, dtype=np.int64)
+            new_rows = True
         elif name == "conc32":
             B = 32 if batch is None else batch
             hi = 32768 if context is None else context
@@ -237,18 +244,26 @@ def make(name: str, seed: int | None = None, device="cpu", *, bf16_subset=False,
             z = torch.randn(B, generator=g, dtype=torch.float64).numpy()
             ctx = np.rint(np.exp(math.log(12000.0) + 1.0 * z)).astype(np.int64)
             ctx = np.clip(ctx, 512, 65536 if context is None else context)
-            if bf16_subset:
-                ctx = ctx[:32]
-                B = len(ctx)
+            new_rows = True
         elif name == "long":
             B = 8 if batch is None else batch
-            ctx = np.full(B, 131072 if context is None else context, dtype=np.int64)
+            ctx = np.full(B, (131072 if context is None else context) - 1, dtype=np.int64)
             dist = "t3"
+            new_rows = True
         else:
             raise KeyError(name)
         n_att = ctx + (1 if new_rows else 0)
         need = int(sum(-(-int(L) // ps) for L in n_att))
         num_pages = need          # the pool holds exactly the pages in use
+        if name == "conc64" and bf16_same_memory:
+            # a BF16 page holds twice the bytes of an FP8 one: the same memory holds half the pages;
+            # sequences are admitted in order while their pages fit
+            num_pages = need // 2
+            pages = np.array([-(-int(L) // ps) for L in n_att])
+            admitted = int(np.searchsorted(np.cumsum(pages), num_pages, side="right"))
+            ctx = ctx[:admitted]
+            B = admitted
+            notes["admitted"] = admitted
 
     att_lens = ctx + (1 if new_rows else 0)
     table, max_pages, n_used = _page_layout(att_lens, ps, num_pages, seed)

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define FP8KV_ABI_VERSION 1
+#define FP8KV_ABI_VERSION 2
 
 /* KV cache element types. */
 #define FP8KV_KV_FP8_E4M3 0 /* 1 byte per element, value = e4m3(code) * scale */
@@ -57,7 +57,7 @@ extern "C" {
 #define FP8KV_ERR_TAGS (-6)        /* exactly one of page_tags / expected_tags given  */
 #define FP8KV_ERR_LAUNCH (-7)      /* the HIP runtime rejected a launch               */
 #define FP8KV_ERR_ALIGN (-8)       /* q/k_new/v_new/caches not 16-byte aligned, out not
-                                      4-byte aligned, or workspace not 256-byte aligned */
+                                      8-byte aligned, or workspace not 256-byte aligned */
 
 /* Abort-flag bits written per sequence by paged_decode_attn. */
 #define FP8KV_ABORT_TAG_MISMATCH 1u /* a used page's tag differs from the expected one */
@@ -79,6 +79,11 @@ const char* fp8kv_last_hip_error(void);
 
 /*
  * kv_quant_append -- write new K/V rows into the paged caches.
+ *
+ * The decode pool keeps its KV cache as e4m3 bytes instead of BF16, so each
+ * new token's K and V are converted once as they enter the cache ("Cloudflare
+ * tối ưu hóa Kimi và GLM trên Workers AI", section "Lượng tử hóa KV cache";
+ * "更小、更快、更安全：大规模运行Kimi和GLM", section "量化 KV 缓存").
  *
  * Row r (of n_rows) belongs to sequence row_seq[r] at token position
  * row_pos[r]; it is written to physical page
@@ -259,6 +264,14 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  * paged_decode_attn -- one decode step of attention for a batch of
  * sequences, one query token each, over a paged FP8 (or BF16) KV cache.
  *
+ * The attention reads the e4m3 cache and converts values as it reads them
+ * ("Cloudflare tối ưu hóa Kimi và GLM trên Workers AI", section "Lượng tử hóa
+ * KV cache"; "更小、更快、更安全：大规模运行Kimi和GLM", section "量化 KV 缓存");
+ * each page's generation tag is compared before the page is used and a
+ * mismatch aborts the request instead of returning wrong data ("ترفندهای
+ * کلادفلر برای جا دادن مدل‌های غول‌پیکر تو GPU", third technique; "Tối ưu hóa
+ * mô hình AI quy mô lớn", section "Bảo vệ tính toàn vẹn của KV Cache").
+ *
  * For sequence b with L = seq_lens[b] cached tokens and query head h
  * (group size G = num_q_heads / num_kv_heads, KV head g = h / G):
  *   k_t  = dequantized K row of token t (t < L) of KV head g,
@@ -271,14 +284,16 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *   q              uint16 BF16 [batch][num_q_heads][head_dim]
  *   k_cache,
  *   v_cache        [num_pages][num_kv_heads][page_size][head_dim]
- *   page_table     int32 [batch][max_pages]; entries past the used pages
- *                  are never read
+ *   page_table     int32 [batch][max_pages]; only the entries of the used
+ *                  pages (slots j < ceil(seq_lens[b] / page_size)) are used as
+ *                  page ids (with tags on, the page check also loads the
+ *                  other entries of the row, without using them)
  *   seq_lens       int32 [batch]
  *   page_tags      uint32 [num_pages]              current page generations
  *   expected_tags  uint32 [batch][max_pages]       generations each sequence
  *                  recorded; both NULL = tag check off (the default), both
  *                  non-NULL = on, one NULL = FP8KV_ERR_TAGS
- *   out            uint16 BF16 [batch][num_q_heads][head_dim]
+ *   out            uint16 BF16 [batch][num_q_heads][head_dim], 8-byte aligned
  *   abort_flags    uint8 [batch]; always written: 0, or an OR of the
  *                  FP8KV_ABORT_* bits
  *   workspace      device buffer of at least
@@ -288,9 +303,6 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *                  results, so calls sharing a workspace must be ordered
  *                  (same stream).
  *
- * A call enqueues two kernels on the stream: the split decode kernel and a
- * merge kernel that combines the partial results of sequences whose work
- * was split between workgroups.
  *   num_blocks     0 = choose automatically (one workgroup per CU, fewer
  *                  for small batches); n > 0 = use n workgroups of 4 waves
  *                  (at most 65535).  The batch's work -- every (sequence,
@@ -301,11 +313,13 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  *                  floating-point rounding, and repeated calls with the same
  *                  inputs and n give bit-identical outputs.
  *
- * A call enqueues three kernels on the stream: a page check (one block per
- * sequence; writes abort_flags), the decode kernel (which reads K/V only of
- * the sequences that passed, so an aborted sequence costs 12 bytes per
- * page), and a merge kernel that combines the partial results of segments
- * split between waves.
+ * Kernels enqueued on the stream: with tags on, a page check (one block per
+ * 1024 page-table slots of a sequence), then the decode kernel, which reads
+ * K/V only of the sequences that passed (an aborted sequence costs 12 bytes
+ * per page) and writes abort_flags, then a merge kernel that combines the
+ * partial results of segments split between waves -- three kernels.  With
+ * tags off there is no page check: the decode checks the lengths and the
+ * page ids of each round of pages before reading any of them -- two kernels.
  *
  * Tag rule: for every page slot j < ceil(L / page_size) (the partial last
  * page included), the page id p = page_table[b*max_pages + j] must lie in
@@ -314,6 +328,14 @@ size_t paged_decode_attn_workspace_size(int32_t batch, int32_t num_q_heads,
  * FP8KV_ABORT_TAG_MISMATCH).  Pages are checked before their contents are
  * used.  When abort_flags[b] != 0, out[b] is NOT WRITTEN (left as it was).
  * The caches are never written.  out must not alias q.
+ *
+ * Errors (nothing launched): FP8KV_ERR_UNSUPPORTED (kv_dtype, head_dim,
+ * page_size, group > FP8KV_MAX_GROUP), FP8KV_ERR_SHAPE (a size <= 0,
+ * num_q_heads not a multiple of num_kv_heads, batch or num_kv_heads above
+ * 65535, max_pages * page_size above INT32_MAX), FP8KV_ERR_NULL,
+ * FP8KV_ERR_TAGS, FP8KV_ERR_SCALE (FP8 scales not finite and positive,
+ * softmax_scale not finite), FP8KV_ERR_ALIGN, FP8KV_ERR_WORKSPACE,
+ * FP8KV_ERR_LAUNCH.
  */
 int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cache,
                       int32_t kv_dtype, float k_scale, float v_scale,
@@ -325,6 +347,48 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t page_size, int32_t num_pages,
                       float softmax_scale, int32_t num_blocks, void* stream);
+
+/*
+ * paged_decode_step -- one whole decode step: kv_quant_append of the step's
+ * new rows (k_new, v_new, row_seq, row_pos, n_rows; n_rows may be 0)
+ * followed by paged_decode_attn, on the same stream, with every argument
+ * meaning what it means there (the append uses page_table, batch,
+ * max_pages, the caches, the scales and kv_dtype of the decode).  The
+ * results are bit-identical to those two calls made in that order.
+ *
+ * The difference is the launches: with tags on, the page check runs in the
+ * append's launch, in blocks of its own beside the append's (the append
+ * writes only cache bytes, the check reads only the page table, lengths
+ * and tags), so a step is three kernels -- append + page check, decode,
+ * merge -- where the two calls make four; with tags off, also three
+ * (append, decode, merge).  The tag check then costs no launch of its own,
+ * which is how a serving loop would run it when tags are on (the pages
+ * give its cost as under 1% of throughput and p95 latency: "ترفندهای
+ * کلادفلر برای جا دادن مدل‌های غول‌پیکر تو GPU", third technique).
+ *
+ *   decode_begin_event,
+ *   decode_end_event   optional hipEvent_t handles (as void*; NULL = none):
+ *                  recorded on `stream` right before the decode kernel and
+ *                  right after it (before the merge), so a caller can time
+ *                  the decode kernel alone.
+ *
+ * Errors: those of paged_decode_attn, then those of kv_quant_append (the
+ * append's pointers are checked only when n_rows > 0).  Nothing is
+ * launched on an error.
+ */
+int paged_decode_step(const uint16_t* k_new, const uint16_t* v_new,
+                      const int32_t* row_seq, const int32_t* row_pos, int32_t n_rows,
+                      const uint16_t* q, void* k_cache, void* v_cache,
+                      int32_t kv_dtype, float k_scale, float v_scale,
+                      const int32_t* page_table, int32_t max_pages,
+                      const int32_t* seq_lens,
+                      const uint32_t* page_tags, const uint32_t* expected_tags,
+                      uint16_t* out, uint8_t* abort_flags,
+                      void* workspace, size_t workspace_bytes,
+                      int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t page_size, int32_t num_pages,
+                      float softmax_scale, int32_t num_blocks,
+                      void* decode_begin_event, void* decode_end_event, void* stream);
 
 /*
  * paged_decode_attn_path -- which kernel family paged_decode_attn uses for a

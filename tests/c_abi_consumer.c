@@ -55,6 +55,16 @@ int main(void) {
   CHECK(decode(NULL, ws, 32, 64, 8, 1.0f, NULL, NULL) == FP8KV_ERR_NULL);         /* no workspace */
   CHECK(decode(dev, ws - 1, 32, 64, 8, 1.0f, NULL, NULL) == FP8KV_ERR_WORKSPACE); /* one byte short */
 
+  /* a whole step: the decode's errors first, then the append's (its rows' pointers only when n_rows > 0) */
+  CHECK(paged_decode_step(NULL, NULL, NULL, NULL, 0, (const uint16_t*)dev, dev, dev, FP8KV_KV_FP8_E4M3, 1.0f, 1.0f,
+                          (const int32_t*)dev, 513, (const int32_t*)dev, NULL, NULL, (uint16_t*)dev, (uint8_t*)dev,
+                          dev, ws - 1, 32, 64, 8, 128, 64, 16416, 0.08838835f, 0, NULL, NULL, NULL) ==
+        FP8KV_ERR_WORKSPACE);
+  CHECK(paged_decode_step(NULL, NULL, NULL, NULL, 32, (const uint16_t*)dev, dev, dev, FP8KV_KV_FP8_E4M3, 1.0f,
+                          1.0f, (const int32_t*)dev, 513, (const int32_t*)dev, NULL, NULL, (uint16_t*)dev,
+                          (uint8_t*)dev, dev, ws, 32, 64, 8, 128, 64, 16416, 0.08838835f, 0, NULL, NULL,
+                          NULL) == FP8KV_ERR_NULL);
+
   /* append: nothing to do is valid (and launches nothing); a head count past the limit is not */
   CHECK(kv_quant_append(NULL, NULL, NULL, NULL, NULL, 1, 1, 1.0f, 1.0f, NULL, NULL, 1, 0, 8, 128, 64,
                         FP8KV_KV_FP8_E4M3, NULL) == FP8KV_OK);

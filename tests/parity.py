@@ -144,6 +144,10 @@ def compare_outputs(gpu_bits, ref, flags, select=None):
     floor = np.abs(_bf16_round(want) - want)
     excess = float((err - floor).max()) if err.size else 0.0
     rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)) if err.size else 0.0
+    raw = float(err.max()) if err.size else 0.0
+    say(f"  margins: max|gpu-oracle| {raw:.3e}, beyond bf16 rounding {excess:.3e} (limit 2e-2), "
+        f"bf16 floor {float(floor.max()) if err.size else 0.0:.3e}, rel-L2 {rel:.3e} (limit 5e-3), "
+        f"|oracle| max {float(np.abs(want).max()) if err.size else 0.0:.3g}")
     assert excess <= ATOL, f"max |gpu - oracle| exceeds 2e-2 beyond bf16 rounding: {excess:.3g}"
     assert rel <= REL_L2, f"relative L2 error {rel:.3g} > 5e-3"
     # aborted sequences: untouched

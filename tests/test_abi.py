@@ -105,11 +105,44 @@ def test_decode_validation_codes(lib):
     assert _decode(lib, vs=-1.0) == E["SCALE"]
     assert _decode(lib, sm=float("nan")) == E["SCALE"]
     assert _decode(lib, q=FAKE + 2) == E["ALIGN"]
+    assert _decode(lib, out=FAKE + 4) == E["ALIGN"]      # out takes 8-byte stores
+    assert _decode(lib, out=FAKE + 2) == E["ALIGN"]
     assert _decode(lib, ws=FAKE + 16) == E["ALIGN"]
     assert _decode(lib, ws_bytes=16) == E["WORKSPACE"]
     assert _decode(lib, max_pages=1 << 28, ps=256) == E["SHAPE"]
     # BF16 ignores the scales, so a zero scale is not an error there: it fails later (workspace)
     assert _decode(lib, kv_dtype=1, ks=0.0, ws_bytes=16) == E["WORKSPACE"]
+
+
+def _step(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, seq=FAKE, pos=FAKE, n_rows=2, q=FAKE, kc=FAKE, vc=FAKE, kv_dtype=0, ks=1.0, vs=1.0,
+             pt=FAKE, max_pages=8, lens=FAKE, tags=None, exp=None, out=FAKE, abort=FAKE, ws=FAKE,
+             ws_bytes=1 << 30, batch=2, hq=8, hkv=2, d=64, ps=16, num_pages=64, sm=0.125, blocks=0, ev0=None,
+             ev1=None)
+    a.update(kw)
+    return lib.paged_decode_step(a["k"], a["v"], a["seq"], a["pos"], a["n_rows"], a["q"], a["kc"], a["vc"],
+                                 a["kv_dtype"], a["ks"], a["vs"], a["pt"], a["max_pages"], a["lens"], a["tags"],
+                                 a["exp"], a["out"], a["abort"], a["ws"], a["ws_bytes"], a["batch"], a["hq"],
+                                 a["hkv"], a["d"], a["ps"], a["num_pages"], a["sm"], a["blocks"], a["ev0"],
+                                 a["ev1"], None)
+
+
+def test_step_validation_codes(lib):
+    # the decode's arguments are checked first, then the append's; nothing is launched on an error
+    E = {n: _header_define("FP8KV_ERR_" + n) for n in
+         ["NULL", "SHAPE", "UNSUPPORTED", "WORKSPACE", "SCALE", "TAGS", "ALIGN"]}
+    assert _step(lib, q=None) == E["NULL"]
+    assert _step(lib, tags=FAKE) == E["TAGS"]
+    assert _step(lib, ws_bytes=16) == E["WORKSPACE"]
+    assert _step(lib, out=FAKE + 4) == E["ALIGN"]
+    assert _step(lib, ks=float("nan")) == E["SCALE"]
+    assert _step(lib, d=96) == E["UNSUPPORTED"]
+    assert _step(lib, k=None) == E["NULL"]                    # rows to append, no rows given
+    assert _step(lib, n_rows=-1) == E["SHAPE"]
+    assert _step(lib, k=FAKE + 8) == E["ALIGN"]
+    assert _step(lib, ws_bytes=16, k=None) == E["WORKSPACE"]  # decode first
+    # with no rows the append's pointers are not needed; this one still fails on the workspace
+    assert _step(lib, n_rows=0, k=None, v=None, seq=None, pos=None, ws_bytes=16) == E["WORKSPACE"]
 
 
 def _append(lib, **kw):

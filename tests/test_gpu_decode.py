@@ -122,6 +122,43 @@ def test_tag_and_metadata_cases(gpu_device):
         compare_outputs(out, ref, flags)
 
 
+INT32_MIN = -2 ** 31
+
+
+@pytest.mark.parametrize("tags_on", [True, False], ids=["tags_on", "tags_off"])
+@pytest.mark.parametrize("num_blocks", [1, 0, 200])
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (8, 2)], ids=["mfma_g8", "valu_g4"])
+def test_bad_metadata_cases(gpu_device, tags_on, num_blocks, hq, hkv):
+    # Every metadata condition the abort rule defines, against the oracle, flags bit-exact and aborted
+    # outputs untouched.  With tags on the page check kernel finds them before the decode; with tags off
+    # the decode's schedule checks the lengths and every wave range-checks each round of page ids before
+    # reading any page.  num_blocks = 1 keeps most segments whole inside one wave; 0 (automatic) and 200
+    # split the long sequence's segments over many waves, so the failing piece is one of several partials.
+    w = W.make_custom([3000, 200, 64, 65, 500, 900, 700, 1, 333], hq, hkv, 128, 16, seed=9, mismatch=[])
+    lens = w.seq_lens.copy()
+    pt = w.page_table.copy()
+    max_tokens = w.max_pages * w.page_size
+    pt[0, 100] = -1                   # a negative id in a used slot of the longest sequence
+    pt[1, 3] = INT32_MIN              # the most negative id
+    lens[2] = max_tokens + 1          # one token more than the table can hold
+    lens[3] = -5                      # a negative length
+    pt[4, 31] = w.num_pages           # the first id past the pool, in the partial last page (500 = 31*16 + 4)
+    pt[5, 60] = -1                    # a bad id beyond the used pages (900 tokens = 57 pages): no abort
+    lens[6] = max_tokens              # the largest valid length, but the row's slots past 44 hold -1
+    lens[8] = INT32_MIN               # the most negative length
+    expect = [2, 2, 2, 2, 2, 0, 2, 0, 2]
+    for kv in (FP8, BF16):
+        say(f"bad metadata kv={kv} tags_on={tags_on} blocks={num_blocks} hq={hq} hkv={hkv}")
+        kc, vc = gpu_fill(w, kv, gpu_device)
+        okc, ovc = oracle_fill(w, kv)
+        out, flags, _ = gpu_decode(w, kv, kc, vc, gpu_device, tags_on=tags_on, num_blocks=num_blocks,
+                                   seq_lens=lens, page_table=pt)
+        ref, rflags = oracle_decode(w, kv, okc, ovc, tags_on=tags_on, seq_lens=lens, page_table=pt)
+        assert rflags.tolist() == expect
+        assert np.array_equal(flags, rflags), f"abort flags {flags.tolist()} != oracle {rflags.tolist()}"
+        compare_outputs(out, ref, flags)
+
+
 @pytest.mark.parametrize("num_blocks", [1, 5])
 def test_mismatch_in_every_page_position(gpu_device, num_blocks):
     # one stale page at a time, in each page slot of a long sequence

@@ -1,6 +1,7 @@
-"""The decode step (kv_quant_append + paged_decode_attn) captured in a HIP
-graph and replayed: the library allocates nothing, never synchronizes and
-issues no memset, so both calls can be captured as they are.  Each replay
+"""The decode step (kv_quant_append + paged_decode_attn, or the one
+paged_decode_step call) captured in a HIP graph and replayed: the library
+allocates nothing, never synchronizes and issues no memset, so the calls can
+be captured as they are.  Each replay
 runs after eager work (new query values, output buffers refilled) and must
 give bit for bit what the same calls give eagerly; the first replay is also
 checked against the oracle."""
@@ -22,7 +23,8 @@ FP8 = fk.KV_FP8_E4M3
 # a batch whose split segments are merged one wave per query head, and one
 # long sequence whose segments spread over many waves (four per query head)
 @pytest.mark.parametrize("lengths", [[3000, 700, 65, 4097, 1], [8192]], ids=["batch5", "one_long"])
-def test_step_replays_in_a_hip_graph(gpu_device, lengths):
+@pytest.mark.parametrize("api", ["two_calls", "step_tags_on", "step_tags_off"])
+def test_step_replays_in_a_hip_graph(gpu_device, lengths, api):
     dev = gpu_device
     w = W.make_custom(lengths, 64, 8, 128, 64, seed=len(lengths) + 7, mismatch=[])
     kc, vc = gpu_fill(w, FP8, dev)
@@ -42,10 +44,17 @@ def test_step_replays_in_a_hip_graph(gpu_device, lengths):
     flags = torch.empty((w.batch,), dtype=torch.uint8, device=dev)
     out_e, flags_e = torch.empty_like(out), torch.empty_like(flags)
 
+    tags_on = api != "step_tags_off"
+
     def step(o, f):
-        fk.kv_quant_append(nk, nv, ns, npos, pt, w.k_scale, w.v_scale, kc, vc, FP8)
-        fk.paged_decode_attn(q, kc, vc, pt, sl, o, f, ws, kv_dtype=FP8, k_scale=w.k_scale, v_scale=w.v_scale,
-                             page_tags=tags, expected_tags=exp, softmax_scale=w.softmax_scale)
+        if api == "two_calls":
+            fk.kv_quant_append(nk, nv, ns, npos, pt, w.k_scale, w.v_scale, kc, vc, FP8)
+            fk.paged_decode_attn(q, kc, vc, pt, sl, o, f, ws, kv_dtype=FP8, k_scale=w.k_scale, v_scale=w.v_scale,
+                                 page_tags=tags, expected_tags=exp, softmax_scale=w.softmax_scale)
+        else:
+            fk.paged_decode_step(nk, nv, ns, npos, q, kc, vc, pt, sl, o, f, ws, kv_dtype=FP8, k_scale=w.k_scale,
+                                 v_scale=w.v_scale, page_tags=tags if tags_on else None,
+                                 expected_tags=exp if tags_on else None, softmax_scale=w.softmax_scale)
 
     side = torch.cuda.Stream(dev)
     side.wait_stream(torch.cuda.current_stream(dev))
@@ -61,7 +70,7 @@ def test_step_replays_in_a_hip_graph(gpu_device, lengths):
 
     gen = torch.Generator().manual_seed(99)
     for r in range(3):
-        say(f"graph replay {r} lengths={lengths}")
+        say(f"graph replay {r} lengths={lengths} api={api}")
         if r > 0:  # new queries: the graph reads the live buffer
             q.copy_(torch.randn(tuple(q.shape), generator=gen).to(torch.bfloat16).to(dev))
         out.view(torch.int16).fill_(OUT_SENTINEL)
@@ -74,7 +83,7 @@ def test_step_replays_in_a_hip_graph(gpu_device, lengths):
         assert torch.equal(out.view(torch.int16), out_e.view(torch.int16)), f"replay {r} differs from eager"
         if r == 0:
             okc, ovc = oracle_fill(w, FP8)
-            ref, rflags = oracle_decode(w, FP8, okc, ovc, tags_on=True)
+            ref, rflags = oracle_decode(w, FP8, okc, ovc, tags_on=tags_on)
             got_flags = flags.cpu().numpy()
             assert np.array_equal(got_flags, rflags)
             compare_outputs(W.bits_u16(out), ref, got_flags)

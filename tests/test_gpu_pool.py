@@ -184,3 +184,74 @@ def test_use_after_free_aborts_the_stale_reader(gpu_device):
     got = W.bits_u16(out[1].cpu())
     from parity import compare_outputs
     compare_outputs(got[None], ref[1:2], np.array([0], np.uint8))
+
+
+def test_corrupt_free_stack_and_bad_counts(gpu_device):
+    # A corrupt free stack hands out ids outside [0, num_pages): page_alloc records them as they are, with
+    # expected tag 0 and no tag write (every array bit-exact with the oracle), and the decode then flags
+    # the sequences that use them (bit 1) and leaves their outputs untouched, tags on and off.  page_free
+    # with a page count outside [0, max_pages] is status 2 and changes nothing.
+    dev = gpu_device
+    hkv, hq, d, ps, batch, max_pages, num_pages = 2, 8, 64, 16, 4, 6, 16
+    say("corrupt free stack")
+    P = Pools(dev, batch, max_pages, num_pages)
+    fc = P.o["free_count"]
+    # pops read entries fc-1, fc-2, ...: sequence 0 gets entries fc-1 and fc-2, sequence 1 the next three
+    for idx, bad in ((fc - 2, num_pages), (fc - 4, -3), (fc - 5, -2 ** 31)):
+        P.o["free_pages"][idx] = bad
+        P.g["free_pages"][idx] = bad
+    tags_before = P.o["tags"].copy()
+    st = P.alloc([2, 3, 1, 0])
+    assert st.tolist() == [0, 0, 0, 0]
+    assert P.o["table"][0, 1] == num_pages and P.o["expected"][0, 1] == 0
+    assert P.o["table"][1, 1] == -3 and P.o["table"][1, 2] == -2 ** 31 and P.o["expected"][1, 2] == 0
+    good = [int(p) for p in P.o["table"][:3].ravel() if 0 <= p < num_pages]
+    changed = np.nonzero(P.o["tags"] != tags_before)[0].tolist()
+    assert sorted(changed) == sorted(good)                      # only the valid pops bumped a tag
+
+    # decode through the pool's table: sequence 0 uses its bad slot 1, sequence 1 its slots 1-2,
+    # sequence 2 only good pages, sequence 3 holds nothing (length 0)
+    lens = np.array([2 * ps, 3 * ps - 5, ps, 0], np.int32)
+    table = P.o["table"].copy()
+    rows_k = torch.randn(batch * max_pages * ps, hkv, d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    rows_v = torch.randn(batch * max_pages * ps, hkv, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    seq = torch.arange(batch, dtype=torch.int32).repeat_interleave(max_pages * ps)
+    pos = torch.arange(max_pages * ps, dtype=torch.int32).repeat(batch)
+    shape = (num_pages, hkv, ps, d)
+    kc = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+    vc = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+    pt = torch.from_numpy(table).to(dev)
+    fk.kv_quant_append(rows_k.to(dev), rows_v.to(dev), seq.to(dev), pos.to(dev), pt, 0.02, 0.02, kc, vc)
+    okc = np.full(shape, 0x7F, np.uint8)
+    ovc = np.full(shape, 0x7F, np.uint8)
+    pa.append(W.bits_u16(rows_k), W.bits_u16(rows_v), seq.numpy(), pos.numpy(), table, 0.02, 0.02, okc, ovc)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_bits(kc), okc) and np.array_equal(pool_bits(vc), ovc)
+    q = torch.randn(batch, hq, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    ws = fk.alloc_workspace(batch, hq, hkv, d, ps, max_pages, device=dev)
+    for tags_on in (True, False):
+        say(f"  decode through the corrupt table, tags_on={tags_on}")
+        out = torch.full((batch, hq, d), 0, dtype=torch.int16, device=dev)
+        out.fill_(0x7FC1)
+        out = out.view(torch.bfloat16)
+        flags = torch.full((batch,), 0xEE, dtype=torch.uint8, device=dev)
+        ws.fill_(0xA5)
+        fk.paged_decode_attn(q.to(dev), kc, vc, pt, torch.from_numpy(lens).to(dev), out, flags, ws,
+                             k_scale=0.02, v_scale=0.02, page_tags=P.g["tags"] if tags_on else None,
+                             expected_tags=P.g["expected"] if tags_on else None)
+        torch.cuda.synchronize()
+        rflags = pa.abort_flags(table, lens, ps, num_pages, P.o["tags"] if tags_on else None,
+                                P.o["expected"] if tags_on else None)
+        assert rflags.tolist() == [2, 2, 0, 2]
+        assert np.array_equal(flags.cpu().numpy(), rflags)
+        ref = pa.decode_attention(W.bits_u16(q), okc, ovc, pa.KV_FP8_E4M3, 0.02, 0.02, table, lens,
+                                  1.0 / np.sqrt(d), flags=rflags)
+        from parity import compare_outputs
+        compare_outputs(W.bits_u16(out.cpu()), ref, rflags)
+
+    say("bad page counts on free")
+    for b, bad in ((0, -1), (1, max_pages + 1), (2, -2 ** 31)):
+        P.o["counts"][b] = bad
+        P.g["counts"][b] = bad
+    st = P.free([1, 1, 1, 1])                                   # compares every array with the oracle
+    assert st.tolist() == [pp.FREE_BAD_COUNT] * 3 + [pp.FREE_OK]
