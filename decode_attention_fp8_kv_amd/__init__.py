@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "KV_FP8_E4M3", "KV_BF16", "ABORT_TAG_MISMATCH", "ABORT_BAD_METADATA", "Fp8KvError",
     "lib_path", "load_library", "abi_version", "kv_quant_append", "paged_decode_attn", "paged_decode_step",
+    "paged_decode_attn_noalloc",
     "paged_decode_attn_workspace_size", "paged_decode_attn_path", "alloc_workspace",
     "kv_quant_append_checked", "page_pool_init", "page_alloc", "page_free", "kv_absmax_scale",
     "kv_absmax_scale_kv",
@@ -32,6 +33,8 @@ ABORT_BAD_METADATA = 2
 AMAX_WORK_FLOATS = 512  # kv_absmax_scale's work buffer, in floats
 INT4_GROUP = 128        # int4_gemv: weights per scale along K
 INT4_MAX_M = 64         # int4_gemv: largest number of activation rows
+NOALLOC_SCRATCH_BYTES = 32 << 20  # paged_decode_attn_noalloc's fixed device scratch
+ERR_SCRATCH = -9        # paged_decode_attn_noalloc: sizes need more than the scratch holds
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libfp8kv.so")
@@ -77,6 +80,9 @@ def load_library() -> ctypes.CDLL:
     lib.paged_decode_attn.restype = c.c_int
     lib.paged_decode_attn.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, vp, sz, i32, i32,
                                       i32, i32, i32, i32, f32, i32, vp]
+    lib.paged_decode_attn_noalloc.restype = c.c_int
+    lib.paged_decode_attn_noalloc.argtypes = [vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32,
+                                              i32, i32, i32, f32, i32, vp]
     lib.paged_decode_step.restype = c.c_int
     lib.paged_decode_step.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, f32, f32, vp, i32, vp, vp, vp, vp, vp,
                                       vp, sz, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp]
@@ -210,6 +216,31 @@ def paged_decode_attn(q, k_cache, v_cache, page_table, seq_lens, out, abort_flag
         batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_blocks),
         _stream_handle(dev, stream))
     _check("paged_decode_attn", status)
+
+
+def paged_decode_attn_noalloc(q, k_cache, v_cache, page_table, seq_lens, out, abort_flags, *,
+                              kv_dtype=KV_FP8_E4M3, k_scale=1.0, v_scale=1.0, page_tags=None, expected_tags=None,
+                              softmax_scale=None, num_blocks=0, stream=None):
+    """paged_decode_attn with the library's fixed device scratch as its workspace (nothing is
+    allocated; calls that overlap on one device race).  See ``paged_decode_attn_noalloc`` in
+    ``include/fp8kv.h``."""
+    dev = q.device
+    batch, hq, d = q.shape
+    num_pages, hkv, page_size, _ = k_cache.shape
+    max_pages = page_table.shape[1]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out.shape != q.shape or abort_flags.numel() != batch or page_table.shape[0] != batch:
+        raise ValueError("shape mismatch")
+    status = load_library().paged_decode_attn_noalloc(
+        _ptr(q, _BF16, "q", dev), _ptr(k_cache, _CACHE[kv_dtype], "k_cache", dev),
+        _ptr(v_cache, _CACHE[kv_dtype], "v_cache", dev), kv_dtype, float(k_scale), float(v_scale),
+        _ptr(page_table, _I32, "page_table", dev), max_pages, _ptr(seq_lens, _I32, "seq_lens", dev),
+        _ptr(page_tags, _U32, "page_tags", dev), _ptr(expected_tags, _U32, "expected_tags", dev),
+        _ptr(out, _BF16, "out", dev), _ptr(abort_flags, (torch.uint8,), "abort_flags", dev),
+        batch, hq, hkv, d, page_size, num_pages, float(softmax_scale), int(num_blocks),
+        _stream_handle(dev, stream))
+    _check("paged_decode_attn_noalloc", status)
 
 
 def _event_handle(ev):

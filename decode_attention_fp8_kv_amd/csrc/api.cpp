@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -117,6 +118,7 @@ const char* fp8kv_status_string(int status) {
     case FP8KV_ERR_TAGS: return "page_tags and expected_tags must both be NULL or both be set";
     case FP8KV_ERR_LAUNCH: return "HIP launch failed (see fp8kv_last_hip_error)";
     case FP8KV_ERR_ALIGN: return "a pointer is not aligned as required";
+    case FP8KV_ERR_SCRATCH: return "the sizes need more workspace than the fixed scratch of the no-allocation call holds";
     default: return "unknown status";
   }
 }
@@ -407,6 +409,82 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                               page_tags, expected_tags, out, abort_flags, workspace, workspace_bytes, batch,
                               num_q_heads, num_kv_heads, head_dim, page_size, num_pages, softmax_scale, num_blocks,
                               p, mfma);
+  if (st != FP8KV_OK) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.checked) {
+    const int e = record_hip(launch_page_check(p, s));
+    if (e != FP8KV_OK) return e;
+  }
+  return record_hip(launch_decode(p, kv_dtype, head_dim, mfma, s));
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------
+// The no-allocation variant of paged_decode_attn.  Its workspace is this
+// file-scope device array: one copy on every device the library runs on,
+// held until the process ends, shared by every call on that device (so
+// calls that overlap on one device race).  Host code never uses the array's
+// name as an address: the device address of the current device's copy is
+// looked up once per device with hipGetSymbolAddress and kept.
+// ------------------------------------------------------------------------
+namespace fp8kv {
+namespace {
+
+constexpr size_t kScratchBytes = FP8KV_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "the workspace is 256-byte aligned");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_address[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return record_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return record_hip(hipErrorInvalidDevice);
+  void* a = g_scratch_address[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    a = g_scratch_address[dev].load(std::memory_order_relaxed);
+    if (a == nullptr) {
+      const hipError_t es = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (es != hipSuccess || a == nullptr) return record_hip(es != hipSuccess ? es : hipErrorInvalidSymbol);
+      g_scratch_address[dev].store(a, std::memory_order_release);
+    }
+  }
+  *out = a;
+  return FP8KV_OK;
+}
+
+}  // namespace
+}  // namespace fp8kv
+
+extern "C" {
+
+int paged_decode_attn_noalloc(const uint16_t* q, const void* k_cache, const void* v_cache, int32_t kv_dtype,
+                              float k_scale, float v_scale, const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens, const uint32_t* page_tags, const uint32_t* expected_tags,
+                              uint16_t* out, uint8_t* abort_flags, int32_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t num_pages,
+                              float softmax_scale, int32_t num_blocks, void* stream) {
+  // Every argument is checked first, against a stand-in workspace address (aligned, never used): a
+  // workspace larger than the scratch is FP8KV_ERR_SCRATCH, and nothing touches the device on an error.
+  DecodeParams p{};
+  bool mfma = false;
+  void* const stand_in = reinterpret_cast<void*>(uintptr_t(256));
+  int st = decode_setup(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_table, max_pages, seq_lens, page_tags,
+                        expected_tags, out, abort_flags, stand_in, kScratchBytes, batch, num_q_heads, num_kv_heads,
+                        head_dim, page_size, num_pages, softmax_scale, num_blocks, p, mfma);
+  if (st == FP8KV_ERR_WORKSPACE) return FP8KV_ERR_SCRATCH;
+  if (st != FP8KV_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != FP8KV_OK) return st;
+  st = decode_setup(q, k_cache, v_cache, kv_dtype, k_scale, v_scale, page_table, max_pages, seq_lens, page_tags,
+                    expected_tags, out, abort_flags, ws, kScratchBytes, batch, num_q_heads, num_kv_heads, head_dim,
+                    page_size, num_pages, softmax_scale, num_blocks, p, mfma);
   if (st != FP8KV_OK) return st;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (p.checked) {

@@ -58,6 +58,8 @@ extern "C" {
 #define FP8KV_ERR_LAUNCH (-7)      /* the HIP runtime rejected a launch               */
 #define FP8KV_ERR_ALIGN (-8)       /* q/k_new/v_new/caches not 16-byte aligned, out not
                                       8-byte aligned, or workspace not 256-byte aligned */
+#define FP8KV_ERR_SCRATCH (-9)     /* paged_decode_attn_noalloc: the sizes need more
+                                      workspace than FP8KV_NOALLOC_SCRATCH_BYTES       */
 
 /* Abort-flag bits written per sequence by paged_decode_attn. */
 #define FP8KV_ABORT_TAG_MISMATCH 1u /* a used page's tag differs from the expected one */
@@ -347,6 +349,41 @@ int paged_decode_attn(const uint16_t* q, const void* k_cache, const void* v_cach
                       int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                       int32_t head_dim, int32_t page_size, int32_t num_pages,
                       float softmax_scale, int32_t num_blocks, void* stream);
+
+/*
+ * paged_decode_attn_noalloc -- paged_decode_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments and results as
+ * paged_decode_attn without the workspace: the call uses the library's own
+ * scratch, a fixed device array of FP8KV_NOALLOC_SCRATCH_BYTES (32 MiB) that
+ * every device the library runs on holds until the process ends.  The call
+ * allocates and frees nothing (no hipMalloc, no allocating library routine);
+ * the first call on a device looks up that device's scratch address once.
+ *
+ * Sizes whose workspace (paged_decode_attn_workspace_size) exceeds the
+ * scratch are rejected with FP8KV_ERR_SCRATCH before anything is launched:
+ * with the automatic grid the decode needs at most ~17 MiB for groups up to
+ * 16 and head_dim 128 on a 256-CU device, plus a few bytes per sequence.
+ * The scratch needs no initialization (every call writes what it reads)
+ * and keeps the last call's contents.  Every call on one device shares that
+ * device's scratch: calls that overlap on one device -- on different
+ * streams, or from different host threads without ordering -- race, so
+ * order them (one stream, or events between streams).
+ *
+ * Errors: those of paged_decode_attn (never FP8KV_ERR_WORKSPACE), plus
+ * FP8KV_ERR_SCRATCH; FP8KV_ERR_LAUNCH if the scratch address cannot be
+ * looked up.
+ */
+#define FP8KV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int paged_decode_attn_noalloc(const uint16_t* q, const void* k_cache, const void* v_cache,
+                              int32_t kv_dtype, float k_scale, float v_scale,
+                              const int32_t* page_table, int32_t max_pages,
+                              const int32_t* seq_lens,
+                              const uint32_t* page_tags, const uint32_t* expected_tags,
+                              uint16_t* out, uint8_t* abort_flags,
+                              int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t page_size, int32_t num_pages,
+                              float softmax_scale, int32_t num_blocks, void* stream);
 
 /*
  * paged_decode_step -- one whole decode step: kv_quant_append of the step's

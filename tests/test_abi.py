@@ -145,6 +145,31 @@ def test_step_validation_codes(lib):
     assert _step(lib, n_rows=0, k=None, v=None, seq=None, pos=None, ws_bytes=16) == E["WORKSPACE"]
 
 
+def test_noalloc_validation_codes(lib):
+    # the no-allocation decode checks every argument before it looks up its scratch; sizes whose
+    # workspace exceeds the fixed scratch are FP8KV_ERR_SCRATCH (nothing launched, no device touched)
+    E = {n: _header_define("FP8KV_ERR_" + n) for n in ["NULL", "SHAPE", "TAGS", "ALIGN", "SCRATCH"]}
+    assert fk.ERR_SCRATCH == E["SCRATCH"]
+    m = re.search(r"#define\s+FP8KV_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", _header_text())
+    assert fk.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, kv_dtype=0, ks=1.0, vs=1.0, pt=FAKE, max_pages=8, lens=FAKE, tags=None,
+                 exp=None, out=FAKE, abort=FAKE, batch=2, hq=8, hkv=2, d=64, ps=16, num_pages=64, sm=0.125,
+                 blocks=65535)
+        a.update(kw)
+        return lib.paged_decode_attn_noalloc(a["q"], a["k"], a["v"], a["kv_dtype"], a["ks"], a["vs"], a["pt"],
+                                             a["max_pages"], a["lens"], a["tags"], a["exp"], a["out"], a["abort"],
+                                             a["batch"], a["hq"], a["hkv"], a["d"], a["ps"], a["num_pages"],
+                                             a["sm"], a["blocks"], None)
+    assert fk.paged_decode_attn_workspace_size(2, 8, 2, 64, 16, 8, 65535) > fk.NOALLOC_SCRATCH_BYTES
+    assert call() == E["SCRATCH"]                   # 65535 blocks: far more partial slots than the scratch holds
+    assert call(q=None) == E["NULL"]
+    assert call(batch=0) == E["SHAPE"]
+    assert call(tags=FAKE) == E["TAGS"]
+    assert call(out=FAKE + 4) == E["ALIGN"]
+
+
 def _append(lib, **kw):
     a = dict(k=FAKE, v=FAKE, seq=FAKE, pos=FAKE, pt=FAKE, batch=2, max_pages=8, ks=1.0, vs=1.0,
              kc=FAKE, vc=FAKE, num_pages=64, n_rows=4, hkv=2, d=64, ps=16, kv_dtype=0)
