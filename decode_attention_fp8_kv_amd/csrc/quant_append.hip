@@ -11,8 +11,24 @@
 // and V: two 16-byte BF16 loads each, one 16-byte (FP8) or two (BF16)
 // stores.  Consecutive threads cover consecutive elements of a row, so loads
 // and stores are fully coalesced; a row of one head is one contiguous run
-// of head_dim elements in its page.  Sixteen independent divisions per
-// tensor and thread keep the IEEE division's dependency chains overlapped.
+// of head_dim elements in its page.
+//
+// The division without dividing: the kernel is bound by its ALU work (the
+// IEEE division's scale/fma/fixup sequence and its quarter-rate reciprocal
+// cost ~27 lane operations per element), so each element is first computed
+// as q1 = fl32(x * r) with r = fl32(1 / s), one multiply.  Two correctly
+// rounded operations put q1 within 2 fp32 ulps of the wanted fl32(x / s)
+// (r normal), and rounding to e4m3 is monotone, so the two give the same code
+// unless an e4m3 rounding midpoint lies within 2 ulps of q1.  For quotients
+// of at least 2^-6 (e4m3's normal range; also the saturation range, where no
+// midpoint exists above 432) the midpoints are the fp32 values whose 20
+// mantissa bits below e4m3's 3 are exactly 1000...0, a fixed-position bit
+// test; quotients in [2^-11, 2^-6), where the e4m3 quantum is the subnormal
+// 2^-9, are not tested and always divided, and below 2^-11 both round to 0.
+// Only flagged elements (a window of +-3 ulps, with a margin) take the IEEE
+// division.  When s is a power of two both quotients are exact products and
+// equal; when r is not a normal fp32 every element is divided.  Checked
+// bit-exact against division on every BF16 pattern at many scales.
 //
 // A decode step's first kernel (append_check_kernel) runs these rows and the
 // page check of the step's decode in one launch: the append writes only
@@ -31,26 +47,92 @@ constexpr int kChunk = 16;  // elements per thread
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 
-// 16 BF16 elements (two 16-byte words) -> 16 e4m3 codes of fp32(x) / s.
-__device__ __forceinline__ u32x4_t quant16(const u32x4_t (&in)[2], float s) {
+// The reciprocal of a scale and whether fl32(x * r) may stand in for
+// fl32(x / s): kNoShortcut when r is not a normal fp32, kExact when s is a
+// power of two (every product is the exact quotient), else kTested.
+enum Shortcut { kTested = 0, kExact = 1, kNoShortcut = 2 };
+struct Recip {
+  float r;
+  Shortcut mode;
+};
+__device__ __forceinline__ Recip reciprocal(float s) {
+  Recip c;
+  c.r = 1.0f / s;  // IEEE, correctly rounded
+  const uint32_t sb = __builtin_bit_cast(uint32_t, s);
+  if (!(c.r >= 1.17549435e-38f && c.r <= 3.40282347e38f))
+    c.mode = kNoShortcut;
+  else if ((sb & 0x7FFFFFu) == 0u && (sb & 0x7F800000u) != 0u)
+    c.mode = kExact;
+  else
+    c.mode = kTested;
+  return c;
+}
+
+constexpr uint32_t kMidWindow = 3;  // fp32 ulps around an e4m3 midpoint that take the division
+
+// fp32 -> e4m3 of a pair known not to hold a NaN: clamp to +-448, then the
+// hardware's round-to-nearest-even conversion.
+__device__ __forceinline__ uint32_t e4m3_encode_pair_finite(float a, float b) {
+  const float ca = __builtin_fminf(__builtin_fmaxf(a, -kE4M3Max), kE4M3Max);
+  const float cb = __builtin_fminf(__builtin_fmaxf(b, -kE4M3Max), kE4M3Max);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false) & 0xFFFFu;
+}
+
+// 16 BF16 elements (two 16-byte words) -> 16 e4m3 codes of fl32(x / s).
+__device__ __forceinline__ u32x4_t quant16(const u32x4_t (&in)[2], float s, const Recip& rc) {
+  float x[16], q[16];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t w = in[i >> 2][i & 3];
+    x[2 * i] = bf16_lo(w);
+    x[2 * i + 1] = bf16_hi(w);
+  }
+  const bool tested = rc.mode == kTested, all = rc.mode == kNoShortcut;  // uniform
+  bool any_nan = false;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    q[i] = x[i] * rc.r;
+    const float a = __builtin_fabsf(q[i]);
+    const bool normal = a >= 0x1p-6f;  // e4m3 normal or saturated range: test the midpoint bits
+    const bool small = a >= 0x1p-11f;  // with !normal: e4m3 subnormal range, always divided
+    const bool near_mid =
+        ((__builtin_bit_cast(uint32_t, q[i]) & 0xFFFFFu) - (0x80000u - kMidWindow)) <= 2u * kMidWindow;
+    // normal implies small: divide iff small and (not normal, or near a midpoint)
+    const bool flag = small & (near_mid | !normal);
+    if (all | (tested & flag)) q[i] = x[i] / s;  // rare: a masked branch
+    if (i & 1) any_nan |= __builtin_isunordered(q[i - 1], q[i]);
+  }
   u32x4_t out;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {  // output word q = elements 4q .. 4q+3
-    const uint32_t w0 = in[q >> 1][2 * (q & 1)], w1 = in[q >> 1][2 * (q & 1) + 1];
-    out[q] = e4m3_encode_pair(bf16_lo(w0) / s, bf16_hi(w0) / s) |
-             (e4m3_encode_pair(bf16_lo(w1) / s, bf16_hi(w1) / s) << 16);
+  for (int w = 0; w < 4; ++w)  // output word w = elements 4w .. 4w+3
+    out[w] = e4m3_encode_pair_finite(q[4 * w], q[4 * w + 1]) |
+             (e4m3_encode_pair_finite(q[4 * w + 2], q[4 * w + 3]) << 16);
+  if (any_nan) {  // NaN inputs (rare): every NaN becomes 0x7F
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      out[w] = e4m3_encode_pair(q[4 * w], q[4 * w + 1]) | (e4m3_encode_pair(q[4 * w + 2], q[4 * w + 3]) << 16);
   }
   return out;
 }
 
-// Thread idx of the append: elements [16 c, 16 c + 16) of one row's
-// num_kv_heads * head_dim, c = idx % (num_kv_heads * head_dim / 16).
+// Thread `threadIdx.x` of append block `blk`: flattened chunk idx = 256 blk +
+// threadIdx.x, i.e. elements [16 c, 16 c + 16) of row idx / cpr's
+// num_kv_heads * head_dim, c = idx % cpr, cpr = num_kv_heads * head_dim / 16.
+// The 64-bit division is done once per block on uniform values; each thread
+// adds its offset and divides a small number (< cpr + 256) by cpr through the
+// fp32 reciprocal, corrected to the exact quotient.
 template <int KV>
-__device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t idx) {
-  const int chunks_per_row = (p.num_kv_heads * p.head_dim) / kChunk;
-  if (idx >= (int64_t)p.n_rows * chunks_per_row) return;
-  const int row = (int)(idx / chunks_per_row);
-  const int e0 = (int)(idx - (int64_t)row * chunks_per_row) * kChunk;  // element within the row
+__device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t blk) {
+  const int cpr = (p.num_kv_heads * p.head_dim) / kChunk;
+  const int64_t base = blk * 256;
+  const int64_t row0 = base / cpr;
+  const int t = (int)(base - row0 * cpr) + (int)threadIdx.x;
+  int extra = (int)((float)t * (1.0f / (float)cpr));
+  extra -= extra * cpr > t ? 1 : 0;
+  extra += (extra + 1) * cpr <= t ? 1 : 0;
+  if (row0 + extra >= p.n_rows) return;
+  const int row = (int)(row0 + extra);
+  const int e0 = (t - extra * cpr) * kChunk;  // element within the row
   const int head = e0 / p.head_dim;
   const int d0 = e0 - head * p.head_dim;
 
@@ -91,8 +173,8 @@ __device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t idx)
     const float ks = p.k_scale_dev != nullptr ? *p.k_scale_dev : p.k_scale;
     const float vs = p.v_scale_dev != nullptr ? *p.v_scale_dev : p.v_scale;
     if (!(ks > 0.f && ks <= 3.40282347e38f && vs > 0.f && vs <= 3.40282347e38f)) return;
-    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = quant16(kin, ks);
-    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = quant16(vin, vs);
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = quant16(kin, ks, reciprocal(ks));
+    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = quant16(vin, vs, reciprocal(vs));
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -104,7 +186,7 @@ __device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t idx)
 
 template <int KV>
 __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
-  append_chunk<KV>(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+  append_chunk<KV>(p, blockIdx.x);
 }
 
 // Blocks [0, append_blocks): the append; then one block per (chunk c,
@@ -114,7 +196,7 @@ template <int KV>
 __global__ __launch_bounds__(256) void append_check_kernel(AppendParams a, DecodeParams d, int64_t append_blocks) {
   const int64_t blk = blockIdx.x;
   if (blk < append_blocks) {
-    append_chunk<KV>(a, blk * 256 + threadIdx.x);
+    append_chunk<KV>(a, blk);
     return;
   }
   const int64_t cb = blk - append_blocks;
