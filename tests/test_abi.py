@@ -36,6 +36,10 @@ def _header_define(name):
 
 @pytest.fixture(scope="module")
 def lib():
+    # FP8KV_TEST_LIB: run these checks against another build of the library (the sanitized host build of
+    # tests/test_abi_sanitized.py)
+    if os.environ.get("FP8KV_TEST_LIB"):
+        fk.lib_path = os.environ["FP8KV_TEST_LIB"]
     return fk.load_library()
 
 
