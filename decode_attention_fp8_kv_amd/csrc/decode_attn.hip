@@ -840,8 +840,10 @@ __device__ __forceinline__ void wave_publish(ValuState<KV, D, GM>& st, const Dec
 // the W = min(4 * num_blocks, TU) waves takes the contiguous unit range
 // [w*TU/W, (w+1)*TU/W), so every wave gets the same work (+-1 unit) --
 // tiles plus piece starts -- whatever the length mix: measured on MI355X, a
-// wave's piece start costs about one tile time, and without the charge the
-// waves that start 5-6 pieces (over several short sequences) ended last.
+// wave's piece start (the query rows, the page ids and the first tile's
+// loads, one after another) costs about 1.6 tile times, and with a charge of
+// one unit the wave that starts 10 pieces over short sequences at batch 64
+// ended ~15 us after the median wave.
 // Each wave derives the schedule itself from seq_lens; the host never reads
 // device memory, and waves never wait for one another.
 //
@@ -858,7 +860,7 @@ constexpr int64_t kSeqCount = int64_t(1) << 44;  // pass 1 packs a sequence coun
 // A segment descriptor with this bit: a page id of the segment failed the
 // decode's range check (tags off); nothing was written for it.
 constexpr uint64_t kDescAbortMeta = uint64_t(1) << 63;
-constexpr int kPieceUnits = 1;                    // schedule units a segment charges at its start
+constexpr int kPieceUnits = 2;                    // schedule units a segment charges at its start
 constexpr int64_t kMinTilesForCharge = 16;        // tiles per wave from which the charge applies
 __device__ __forceinline__ int64_t range_start(int64_t w, int64_t total, int64_t nw) { return w * total / nw; }
 // the wave whose range holds flattened unit x

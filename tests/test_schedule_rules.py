@@ -2,7 +2,7 @@
 the invariants the kernel relies on (CPU only).
 
 Rules (as the kernel applies them per call): each sequence with T > 0 tiles
-contributes num_kv_heads segments of delta + T units -- delta = 1 start
+contributes num_kv_heads segments of delta + T units -- delta = 2 start
 charge when the waves average at least 16 tiles, else 0 -- laid out
 sequence-major; wave w of W = min(4 * num_blocks, total units) owns units
 [w*TU/W, (w+1)*TU/W); a wave's range cut at segment boundaries gives its
@@ -24,7 +24,7 @@ import numpy as np
 import pytest
 
 
-def _check(T_list, hkv, nb, piece_units=1, min_tiles=16):
+def _check(T_list, hkv, nb, piece_units=2, min_tiles=16):
     max_waves = 4 * nb
     TT = sum(T_list) * hkv
     n_segs = sum(1 for t in T_list if t > 0) * hkv
