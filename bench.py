@@ -608,9 +608,11 @@ PROFILE_CMDS = {
     "trace_next": "rocprofv3 --kernel-trace --stats -f csv -d OUT/trace_next -o run -- python3 bench.py --next-only",
     "fetch_next": "rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/pmc_fetch_next -o run -- python3 bench.py --next-only",
     "write_next": "rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/pmc_write_next -o run -- python3 bench.py --next-only",
-    "sq": "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD "
+    "sq": "rocprofv3 --pmc SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_VMEM_RD "
           "SQ_WAVES SQ_WAIT_INST_ANY SQ_ACTIVE_INST_ANY -f csv -d OUT/pmc_sq -o run -- "
           "python3 bench.py --workload conc64 --decode-only --no-tag-ab --no-bf16 --steps 10 --warmup 5",
+    "lds": "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS -f csv -d OUT/pmc_lds -o run -- "
+           "python3 bench.py --workload conc64 --decode-only --no-tag-ab --no-bf16 --steps 10 --warmup 5",
     "tcc": "rocprofv3 --pmc TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_sum -f csv -d OUT/pmc_tcc -o run -- "
            "python3 bench.py --workload conc64 --decode-only --no-tag-ab --no-bf16 --steps 10 --warmup 5",
 }
@@ -801,7 +803,9 @@ def summarize_sq_tcc(out_dir: str) -> None:
     """Instruction mix, LDS conflicts and L2 hit rate of the FP8 decode kernel (per dispatch), headline workload."""
     from collections import defaultdict
     vals = defaultdict(lambda: defaultdict(float))
-    for sub_dir in ("pmc_sq", "pmc_tcc"):
+    for sub_dir in ("pmc_sq", "pmc_tcc", "pmc_lds"):
+        if not os.path.isdir(os.path.join(out_dir, sub_dir)):
+            continue
         for r in _csv_rows(os.path.join(out_dir, sub_dir, "run_counter_collection.csv")):
             if _short(r["Kernel_Name"]) == DECODE_KERNEL[0]:
                 vals[r["Counter_Name"]][(sub_dir, r["Dispatch_Id"])] += float(r["Counter_Value"])
@@ -813,12 +817,22 @@ def summarize_sq_tcc(out_dir: str) -> None:
            "# conflicts and L2 hits, per dispatch, from two rocprofv3 counter passes (repository root; OUT any folder):",
            "#   export TMPDIR=/tmp && " + PROFILE_CMDS["sq"],
            "#   export TMPDIR=/tmp && " + PROFILE_CMDS["tcc"],
+           "#   export TMPDIR=/tmp && " + PROFILE_CMDS["lds"],
+           "# (a counter read in two passes is averaged over both; SQ_LDS_BANK_CONFLICT has a pass of its own:",
+           "# collected beside seven other SQ counters it read the same value as SQ_INSTS_MFMA)",
            f"kernel_source_hash: {kernel_source_hash()}"]
     for k in sorted(avg):
         out.append(f"{k}: {avg[k]:.0f}")
-    if avg.get("SQ_INSTS_LDS"):
+    if avg.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in avg:
         out.append(f"lds_bank_conflict_cycles_per_lds_instruction: "
-                   f"{avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_INSTS_LDS']:.3f}")
+                   f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_INSTS_LDS']:.3f}")
+    tiles_ok = avg.get("SQ_INSTS_MFMA", 0.0) / 32.0   # 32 MFMAs per (sequence, KV head, tile) on this path
+    if tiles_ok:
+        out.append(f"tiles_decoded_per_dispatch: {tiles_ok:.0f}   # SQ_INSTS_MFMA / 32")
+        if "SQ_INSTS_VALU" in avg:
+            out.append(f"valu_instructions_per_tile: {avg['SQ_INSTS_VALU'] / tiles_ok:.0f}")
+        if "SQ_INSTS_VMEM_RD" in avg:
+            out.append(f"vmem_read_instructions_per_tile: {avg['SQ_INSTS_VMEM_RD'] / tiles_ok:.1f}")
     if avg.get("TCC_HIT_sum", 0) + avg.get("TCC_MISS_sum", 0) > 0:
         out.append(f"l2_hit_rate: {avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.4f}")
     out.append(f"# (tiles of all sequences, aborted ones included: {tiles}; the decode streams only the others)")
