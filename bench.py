@@ -814,12 +814,12 @@ def summarize_sq_tcc(out_dir: str) -> None:
     w = W.make(WORKLOAD)
     tiles = sum(-(-int(L) // 64) for L in w.seq_lens) * w.num_kv_heads   # upper bound: aborted ones included
     out = [f"# {DECODE_KERNEL[0]} (FP8 cache) on the {WORKLOAD} workload: instruction mix, LDS bank",
-           "# conflicts and L2 hits, per dispatch, from two rocprofv3 counter passes (repository root; OUT any folder):",
+           "# conflicts and L2 hits, per dispatch, from three rocprofv3 counter passes (repository root; OUT any folder):",
            "#   export TMPDIR=/tmp && " + PROFILE_CMDS["sq"],
            "#   export TMPDIR=/tmp && " + PROFILE_CMDS["tcc"],
            "#   export TMPDIR=/tmp && " + PROFILE_CMDS["lds"],
-           "# (a counter read in two passes is averaged over both; SQ_LDS_BANK_CONFLICT has a pass of its own:",
-           "# collected beside seven other SQ counters it read the same value as SQ_INSTS_MFMA)",
+           "# (a counter read in two passes is averaged over both; SQ_LDS_BANK_CONFLICT, in cycles, has a pass",
+           "# of its own; it equals SQ_INSTS_MFMA here because both come to 32 per tile)",
            f"kernel_source_hash: {kernel_source_hash()}"]
     for k in sorted(avg):
         out.append(f"{k}: {avg[k]:.0f}")
@@ -833,6 +833,10 @@ def summarize_sq_tcc(out_dir: str) -> None:
             out.append(f"valu_instructions_per_tile: {avg['SQ_INSTS_VALU'] / tiles_ok:.0f}")
         if "SQ_INSTS_VMEM_RD" in avg:
             out.append(f"vmem_read_instructions_per_tile: {avg['SQ_INSTS_VMEM_RD'] / tiles_ok:.1f}")
+        if "SQ_INSTS_LDS" in avg:
+            out.append(f"lds_instructions_per_tile: {avg['SQ_INSTS_LDS'] / tiles_ok:.1f}")
+        if "SQ_LDS_BANK_CONFLICT" in avg:
+            out.append(f"lds_bank_conflict_cycles_per_tile: {avg['SQ_LDS_BANK_CONFLICT'] / tiles_ok:.1f}")
     if avg.get("TCC_HIT_sum", 0) + avg.get("TCC_MISS_sum", 0) > 0:
         out.append(f"l2_hit_rate: {avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.4f}")
     out.append(f"# (tiles of all sequences, aborted ones included: {tiles}; the decode streams only the others)")
