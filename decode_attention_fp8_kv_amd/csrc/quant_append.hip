@@ -161,11 +161,21 @@ __device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t blk)
   const int64_t dst = (((int64_t)page * p.num_kv_heads + head) * page_size + slot) * p.head_dim + d0;
   const int64_t src = (int64_t)row * p.num_kv_heads * p.head_dim + e0;
 
+  // FP8: the thread's 16 elements are contiguous (one 16-byte store).  BF16:
+  // elements [8c, 8c + 8) and [D/2 + 8c, +8) of its head (c = d0 / 16), so
+  // that each of its two 16-byte stores lines up with its neighbours' into
+  // whole lines.  The cache is written with non-temporal stores (streamed
+  // past the caches: the append's rows are not read back by this kernel);
+  // with two adjacent 16-byte stores per thread each store instruction
+  // covered half of every line and the non-temporal BF16 append ran at 4.1
+  // TB/s instead of 5.5.
+  const int64_t piece = KV == 0 ? 8 : p.head_dim / 2;
+  const int64_t shift = KV == 0 ? 0 : -(d0 / 2);
   u32x4_t kin[2], vin[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    kin[h] = *reinterpret_cast<const u32x4_t*>(p.k_new + src + 8 * h);
-    vin[h] = *reinterpret_cast<const u32x4_t*>(p.v_new + src + 8 * h);
+    kin[h] = *reinterpret_cast<const u32x4_t*>(p.k_new + src + shift + piece * h);
+    vin[h] = *reinterpret_cast<const u32x4_t*>(p.v_new + src + shift + piece * h);
   }
   if constexpr (KV == 0) {
     // Device-scale append: the scales come from device memory (a scale that
@@ -173,13 +183,17 @@ __device__ __forceinline__ void append_chunk(const AppendParams& p, int64_t blk)
     const float ks = p.k_scale_dev != nullptr ? *p.k_scale_dev : p.k_scale;
     const float vs = p.v_scale_dev != nullptr ? *p.v_scale_dev : p.v_scale;
     if (!(ks > 0.f && ks <= 3.40282347e38f && vs > 0.f && vs <= 3.40282347e38f)) return;
-    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst) = quant16(kin, ks, reciprocal(ks));
-    *reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst) = quant16(vin, vs, reciprocal(vs));
+    __builtin_nontemporal_store(quant16(kin, ks, reciprocal(ks)),
+                                reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.k_cache) + dst));
+    __builtin_nontemporal_store(quant16(vin, vs, reciprocal(vs)),
+                                reinterpret_cast<u32x4_t*>(static_cast<uint8_t*>(p.v_cache) + dst));
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.k_cache) + dst + 8 * h) = kin[h];
-      *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.v_cache) + dst + 8 * h) = vin[h];
+      __builtin_nontemporal_store(kin[h], reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.k_cache) + dst + shift +
+                                                                     piece * h));
+      __builtin_nontemporal_store(vin[h], reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.v_cache) + dst + shift +
+                                                                     piece * h));
     }
   }
 }
