@@ -97,22 +97,24 @@ def test_append_fp8_all_bf16_patterns_many_scales(gpu_device, scale):
     assert badv.size == 0, f"{badv.size} V bytes differ, first at {badv[:5]}"
 
 
-def test_append_bf16_copies_bits(gpu_device):
-    say("append bf16 copy all patterns")
-    hkv, d, ps = 2, 64, 16
+@pytest.mark.parametrize("hkv,d,ps", [(2, 64, 16), (8, 128, 64)])
+def test_append_bf16_copies_bits(gpu_device, hkv, d, ps):
+    say(f"append bf16 copy all patterns hkv={hkv} d={d} ps={ps}")
     t, rows = _all_bf16_rows(hkv, d)
+    vrows = np.ascontiguousarray(rows[::-1, :, ::-1])     # V: the same patterns in another order
+    tv = torch.from_numpy(vrows.view(np.int16)).view(torch.bfloat16)
     pt, seq, pos, pool = _layout(rows.shape[0], ps, 4, seed=3)
     shape = (pool, hkv, ps, d)
     fill = torch.tensor(0x1234, dtype=torch.int16).view(torch.bfloat16).item()
     kc = torch.full(shape, fill, dtype=torch.bfloat16, device=gpu_device)
     vc = torch.full(shape, fill, dtype=torch.bfloat16, device=gpu_device)
-    fk.kv_quant_append(t.to(gpu_device), t.to(gpu_device), torch.from_numpy(seq).to(gpu_device),
+    fk.kv_quant_append(t.to(gpu_device), tv.to(gpu_device), torch.from_numpy(seq).to(gpu_device),
                        torch.from_numpy(pos).to(gpu_device), torch.from_numpy(pt).to(gpu_device),
                        1.0, 1.0, kc, vc, fk.KV_BF16)
     torch.cuda.synchronize()
     okc = np.full(shape, 0x1234, np.uint16)
     ovc = np.full(shape, 0x1234, np.uint16)
-    pa.append(rows, rows, seq, pos, pt, 1.0, 1.0, okc, ovc, pa.KV_BF16)
+    pa.append(rows, vrows, seq, pos, pt, 1.0, 1.0, okc, ovc, pa.KV_BF16)
     assert np.array_equal(pool_bits(kc), okc) and np.array_equal(pool_bits(vc), ovc)
 
 
