@@ -7,16 +7,20 @@
 // Each element x becomes e4m3(fp32(x) / scale): an IEEE fp32 division, then
 // round-to-nearest-even with saturation at +-448.
 //
-// One thread moves 16 consecutive elements of one (row, KV head) for both K
-// and V: two 16-byte BF16 loads each, one 16-byte (FP8) or two (BF16)
-// stores.  Consecutive threads cover consecutive elements of a row, so loads
+// One thread moves 16 elements of one (row, KV head) for both K and V, two
+// 16-byte BF16 loads each: 16 consecutive elements and one 16-byte store
+// with an FP8 cache; with a BF16 cache two runs of 8 half a head apart and
+// two 16-byte stores, so that each store instruction of a wave writes whole
+// lines.  Consecutive threads cover consecutive elements of a row, so loads
 // and stores are fully coalesced; a row of one head is one contiguous run
-// of head_dim elements in its page.
+// of head_dim elements in its page.  The cache is written with non-temporal
+// stores: the kernel is bound by HBM's mixed read/write rate.
 //
-// The division without dividing: the kernel is bound by its ALU work (the
-// IEEE division's scale/fma/fixup sequence and its quarter-rate reciprocal
-// cost ~27 lane operations per element), so each element is first computed
-// as q1 = fl32(x * r) with r = fl32(1 / s), one multiply.  Two correctly
+// The division without dividing: with an IEEE division per element the
+// kernel was bound by its ALU work (the division's scale/fma/fixup sequence
+// and its quarter-rate reciprocal cost ~27 lane operations per element), so
+// each element is first computed as q1 = fl32(x * r) with r = fl32(1 / s),
+// one multiply.  Two correctly
 // rounded operations put q1 within 2 fp32 ulps of the wanted fl32(x / s)
 // (r normal), and rounding to e4m3 is monotone, so the two give the same code
 // unless an e4m3 rounding midpoint lies within 2 ulps of q1.  For quotients
