@@ -16,18 +16,17 @@
 // of head_dim elements in its page.  The cache is written with non-temporal
 // stores: the kernel is bound by HBM's mixed read/write rate.
 //
-// The division without dividing: with an IEEE division per element the
-// kernel was bound by its ALU work (the division's scale/fma/fixup sequence
-// and its quarter-rate reciprocal cost ~27 lane operations per element), so
-// each element is first computed as q1 = fl32(x * r) with r = fl32(1 / s),
-// one multiply.  Two correctly
-// rounded operations put q1 within 2 fp32 ulps of the wanted fl32(x / s)
-// (r normal), and rounding to e4m3 is monotone, so the two give the same code
-// unless an e4m3 rounding midpoint lies within 2 ulps of q1.  For quotients
-// of at least 2^-6 (e4m3's normal range; also the saturation range, where no
-// midpoint exists above 432) the midpoints are the fp32 values whose 20
-// mantissa bits below e4m3's 3 are exactly 1000...0, a fixed-position bit
-// test; quotients in [2^-11, 2^-6), where the e4m3 quantum is the subnormal
+// The division without dividing: with an IEEE division per element the kernel
+// was bound by its ALU work (the division's scale/fma/fixup sequence and its
+// quarter-rate reciprocal cost ~27 lane operations per element), so each
+// element is first computed as q1 = fl32(x * r) with r = fl32(1 / s), one
+// multiply.  Two correctly rounded operations put q1 within 2 fp32 ulps of the
+// wanted fl32(x / s) (r normal), and rounding to e4m3 is monotone, so the two
+// give the same code unless an e4m3 rounding midpoint lies within 2 ulps of q1.
+// For quotients of at least 2^-6 (e4m3's normal range; also the saturation
+// range, where no midpoint exists above 432) the midpoints are the fp32 values
+// whose 20 mantissa bits below e4m3's 3 are exactly 1000...0, a fixed-position
+// bit test; quotients in [2^-11, 2^-6), where the e4m3 quantum is the subnormal
 // 2^-9, are not tested and always divided, and below 2^-11 both round to 0.
 // Only flagged elements (a window of +-3 ulps, with a margin) take the IEEE
 // division.  When s is a power of two both quotients are exact products and
