@@ -75,11 +75,37 @@ def counters_path(wl: str, kv_name: str) -> str:
     return os.path.join(ROOT, "profiles", f"decode_kernel_{wl}_{kv_name}_counters.txt")
 
 
+def _code_only(text: str) -> str:
+    """C/C++/HIP source without its comments and with whitespace runs collapsed:
+    what the compiler sees, so that a comment edit does not invalidate a profile."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                            # string or character literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(sources=None) -> str:
+    """Hash of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for rel in sources or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
