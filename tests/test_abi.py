@@ -7,7 +7,6 @@
 * the workspace-size function is deterministic and grows with the problem.
 """
 
-import ctypes
 import os
 import re
 

@@ -12,7 +12,6 @@ is needed; a sanitizer report fails the test.
 
 import glob
 import os
-import shutil
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
