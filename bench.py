@@ -18,8 +18,9 @@ count).  Beside it: the BF16-cache run in a pool of the same bytes (it admits
 per launch / mean kernel time from HIP events recorded right before and after
 it on the launch stream), the whole step's time, the other workloads (batch
 32, batch 1 at 32k, batch 8 at 131k) with the same figures, the tag-check
-overhead against calls with no check at all, and the CPU oracle's rate on a
-bounded sample of the headline workload.
+overhead against calls with no check at all, the legs of the page pool, the
+prefill hand-off and the INT4 GEMV, and the CPU oracle's rate on a bounded
+sample of the headline workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
   python bench.py --workload conc64|conc32|latency|long --decode-only
