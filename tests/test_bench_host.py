@@ -1,5 +1,7 @@
 """Host logic of bench.py that needs no GPU: the kernel-source hash that ties a
-committed profile to the code it measured, and the one-GPU rule."""
+committed profile to the code it measured, the counter summary's scaling of
+rocprofv3 FETCH_SIZE / WRITE_SIZE by the device copy (checked by hand on a
+synthetic pair of counter passes), and the one-GPU rule."""
 
 import os
 import shutil
@@ -50,3 +52,55 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _write_counter_csv(path, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for i, (kernel, counter, value) in enumerate(rows):
+            w.writerow([i, kernel, counter, value])
+
+
+def test_counter_summary_scales_by_the_device_copy_and_reads_back(tmp_path, monkeypatch):
+    # A synthetic pair of counter passes: the 2 GiB device copy reads as 1 GiB fetched and 2 GiB written
+    # (factors 2 and 1, as on the device), two decode dispatches, one append + check, one merge.
+    assert bench.COPY_BYTES == 2 * 1024 ** 3
+    copy = "__amd_rocclr_copyBuffer"
+    dec = "void fp8kv::(anonymous namespace)::decode_kernel<0, 128, 16, true>(fp8kv::DecodeParams)"
+    app = "void fp8kv::(anonymous namespace)::append_check_kernel<0>(fp8kv::AppendParams, fp8kv::DecodeParams, long)"
+    mrg = "void fp8kv::(anonymous namespace)::merge_kernel<128, 1>(fp8kv::DecodeParams)"
+    out = tmp_path / "run"
+    _write_counter_csv(str(out / "pmc_fetch_conc32" / "run_counter_collection.csv"),
+                       [(copy, "FETCH_SIZE", 1048576), (dec, "FETCH_SIZE", 1000), (dec, "FETCH_SIZE", 1200),
+                        (app, "FETCH_SIZE", 5), (mrg, "FETCH_SIZE", 20)])
+    _write_counter_csv(str(out / "pmc_write_conc32" / "run_counter_collection.csv"),
+                       [(copy, "WRITE_SIZE", 2097152), (dec, "WRITE_SIZE", 10), (dec, "WRITE_SIZE", 10),
+                        (app, "WRITE_SIZE", 3), (mrg, "WRITE_SIZE", 4)])
+    (out / "pmc_fetch_conc32" / "line.json").write_text(
+        '{"legs": {"fp8": {"alg_bytes_decode": 2000000, "alg_bytes_step": 2100000}}}')
+    written = {}
+    monkeypatch.setattr(bench, "counters_path",
+                        lambda wl, kv: written.setdefault((wl, kv), str(tmp_path / f"{wl}_{kv}.txt")))
+    bench.summarize_workload_counters(str(out), "conc32")
+    assert list(written) == [("conc32", "fp8")]          # no BF16 leg in the line: no BF16 summary
+    vals = {}
+    for ln in open(written[("conc32", "fp8")]):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            vals[k.strip()] = v.strip()
+    assert float(vals["fetch_scale"]) == 2.0 and float(vals["write_scale"]) == 1.0
+    dec_bytes = 1100 * 1024 * 2 + 10 * 1024             # mean FETCH x 2 + mean WRITE x 1
+    step_bytes = dec_bytes + (5 * 1024 * 2 + 3 * 1024) + (20 * 1024 * 2 + 4 * 1024)
+    assert int(vals["decode_traffic_bytes_per_launch"]) == dec_bytes
+    assert int(vals["step_traffic_bytes"]) == step_bytes
+    assert float(vals["decode_traffic_over_algorithmic"]) == pytest.approx(dec_bytes / 2000000, abs=1e-4)
+    assert float(vals["step_traffic_over_algorithmic"]) == pytest.approx(step_bytes / 2100000, abs=1e-4)
+    # the bench reads the traffic back only while the summary's source hash is the current one
+    assert bench.read_traffic("conc32", "fp8") == dec_bytes
+    path = written[("conc32", "fp8")]
+    text = open(path).read().replace(bench.kernel_source_hash(), "0000000000000000")
+    open(path, "w").write(text)
+    assert bench.read_traffic("conc32", "fp8") is None
